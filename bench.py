@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Throughput of fused linear cross-entropy forward+backward on one MI355X.
+
+One step = one ``flce_fwd_bwd`` call over the whole batch: logits GEMM with the
+fused softcap / log-sum-exp / argmax epilogue, row merge, grad logits, the
+grad_h and grad_W GEMMs, for every token chunk, and the loss/n_correct
+finalisation.  Inputs are seeded synthetic tensors (``synth``) already resident
+in HBM when the timed region starts.
+
+Prints one JSON line (rank 0) with the metric, a roofline entry for the
+dominant kernel (its average launch duration measured with HIP events on its
+own stream during the timed steps) and the fp64 oracle timed on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FLCE fwd+bwd tokens/sec at V=202048,H=6656 bf16; % of MFMA bf16 peak"
+# MI355X dense MFMA peaks (TFLOP/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+GEMM_KINDS = ("fwd_logits", "grad_h", "grad_W")
+
+WORKLOAD_TEXT = {
+    "c1": "fp32 small: N=256, H=128, V=1024, 10% ignore_index, mean",
+    "c2": "bf16 lm_head: N=4096, H=4096, V=128256, 5% ignore_index, mean",
+    "c3": "bf16 DeepSeek-V3-shaped lm_head: N=8192, H=7168, V=129280, Zipf(1.1) labels, 5% ignore_index, mean",
+    "c4": "bf16 Muse-Glimmer-shaped lm_head: N=8192, H=6656, V=202048, softcap T=30, multiplier 0.5, "
+          "uniform labels, 5% ignore_index, mean, n_correct",
+    "c5": "bf16 long context: N=32768 (4 x 8192), H=7168, V=129280, softcap T=30, Zipf(1.1) labels, "
+          "20% ignore_index as tail padding, sum",
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(case, n_tokens: int) -> dict:
+    """The fp64 oracle, as it stands, on the first n_tokens rows of the same
+    inputs: full forward and backward for those rows."""
+    import oracle
+    import synth
+    cfg = case.cfg
+    n = min(n_tokens, cfg.N)
+    h = case.h_f32()[:n]
+    W = case.W_f32()
+    lab = case.labels[:n]
+    t0 = time.perf_counter()
+    oracle.flce_reference(h, W, lab, synth.IGNORE_INDEX, cfg.softcap_T, cfg.multiplier, cfg.reduction)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {cfg.N} tokens of the same seeded inputs, full fp64 forward+backward "
+                      f"(loss, argmax, grad_h rows, the sample's [V,H] grad_W) in {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c4", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cpu-tokens", type=int, default=192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is a design note, not part of this build", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import linear_cross_entropy_gemm_amd as L
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    log(f"[bench] generating {args.config} inputs ...")
+    case = synth.make_case(cfg)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f}s")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if cfg.dtype == "bf16":
+        h = torch.from_numpy(case.h.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(case.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        h = torch.from_numpy(case.h).to(dev)
+        W = torch.from_numpy(case.W).to(dev)
+    lab = torch.from_numpy(case.labels).to(dev)
+    softcap = cfg.softcap_T if cfg.softcap_T > 0 else None
+    kw = dict(softcap=softcap, multiplier=cfg.multiplier, reduction=cfg.reduction)
+    dtype_code = L.FLCE_DTYPE_BF16 if cfg.dtype == "bf16" else L.FLCE_DTYPE_F32
+    plan = L.flce_plan(cfg.N, cfg.H, cfg.V, dtype_code)
+    log(f"[bench] plan {plan.as_dict()}")
+
+    o = L.fwd_bwd(h, W, lab, **kw)                      # allocates outputs + workspace, checks status
+    ws = o.workspace
+    for i in range(args.warmup):
+        L.fwd_bwd(h, W, lab, workspace=ws, out=o, check=False, **kw)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); loss {o.loss.item():.6f} n_correct {o.n_correct.item()}")
+
+    stream = torch.cuda.current_stream(dev)
+    L.flce_profile_enable(True)
+    L.flce_profile_read(stream.cuda_stream, reset=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        L.fwd_bwd(h, W, lab, workspace=ws, out=o, check=False, **kw)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    prof = L.flce_profile_read(stream.cuda_stream, reset=True)
+    L.flce_profile_enable(False)
+    st = L.flce_read_status(ws.data_ptr(), stream.cuda_stream)
+    if st != L.FLCE_OK:
+        raise L.FlceError(st, "device status after timing")
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tok_s = cfg.N / (ms * 1e-3)
+    flops = 6.0 * cfg.N * cfg.H * cfg.V
+    flops_valid = 6.0 * cfg.n_valid * cfg.H * cfg.V
+    peak = PEAK_TFLOPS[cfg.dtype]
+    pct = flops / (ms * 1e-3) / (peak * 1e12) * 100.0
+    pct_valid = flops_valid / (ms * 1e-3) / (peak * 1e12) * 100.0
+    log(f"[bench] {ms:.3f} ms/step, {tok_s:,.0f} tokens/s, {pct:.1f}% of MFMA peak "
+        f"(6NHV basis; {pct_valid:.1f}% on 6*N_valid*H*V)")
+
+    kernels = {}
+    for k, (tot, n) in prof.items():
+        if n:
+            kernels[k] = {"avg_ms": tot / n, "launches_per_step": n / args.steps,
+                          "ms_per_step": tot / args.steps}
+            log(f"[bench]   {k:14s} {tot / args.steps:8.3f} ms/step  {n / args.steps:4.1f} launches  "
+                f"{tot / n:8.3f} ms avg")
+    dom = max((k for k in kernels if k in GEMM_KINDS), key=lambda k: kernels[k]["ms_per_step"])
+    flops_per_launch = 2.0 * cfg.N * cfg.H * cfg.V / kernels[dom]["launches_per_step"]
+    achieved = flops_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "flops_per_launch": flops_per_launch, "avg_launch_ms": round(kernels[dom]["avg_ms"], 4)}
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "N": cfg.N, "H": cfg.H,
+                   "V": cfg.V, "n_valid": cfg.n_valid, "softcap_T": cfg.softcap_T,
+                   "multiplier": cfg.multiplier, "reduction": cfg.reduction,
+                   "chunk_rows": plan.chunk_rows, "n_chunks": plan.n_chunks, "split_k": plan.split_k,
+                   "parallelism": "single GPU"},
+        "pct_peak_6NHV": round(pct, 2), "pct_peak_6NvalidHV": round(pct_valid, 2),
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on {args.cpu_tokens} tokens (host cores) ...")
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_tokens)
+        log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,180 @@
+/*
+ * flce.h -- C ABI of the MI355X (gfx950) fused linear cross-entropy library.
+ *
+ * Fused linear cross-entropy (FLCE) is the lm_head projection of hidden states
+ * onto the vocabulary fused with the cross-entropy loss and its backward pass,
+ * so that the [tokens, vocab] logits tensor is never materialised:
+ *   - Liger-Kernel commit e6a81bb0c3 ("Muse Glimmer" support), Summary item 1
+ *     (fused linear + cross-entropy / skip-logits path), Summary item 2 (token
+ *     accuracy), Details > Softcap (T * tanh(logits * m / T), with the output
+ *     multiplier m folded onto the hidden-state side), Memory (fp32
+ *     [vocab, hidden] weight-gradient accumulator);
+ *   - Liger-Kernel commit 40a9d8a61b ("DeepSeek-V3" support), Summary (logits
+ *     never materialised in training with labels) and Memory (chunked
+ *     transients plus a fixed fp32 weight-gradient accumulator).
+ *
+ * Per call, for N tokens with hidden size H and vocabulary V:
+ *   a     = m * (h W^T)                          [N, V], never stored whole
+ *   z     = T * tanh(a / T)     (T > 0), else a
+ *   lse_i = log sum_v exp(z_iv)
+ *   loss  = s * sum_{valid i} (lse_i - z_{i, label_i}),
+ *           s = 1 / N_valid (mean; 0 if N_valid = 0) or 1 (sum)
+ *   pred_i = lowest v with z_iv = max_v z_iv;  n_correct = #{valid i : pred_i = label_i}
+ *   G_iv  = s * (softmax(z_i)_v - [v = label_i]) * (1 - (z_iv / T)^2)  on valid rows, 0 otherwise
+ *   grad_h = m * G W        [N, H], dtype of h
+ *   grad_W = m * G^T h      [V, H], fp32 (overwritten, not accumulated)
+ * A row is valid when label_i != ignore_index.  The upstream gradient of the
+ * scalar loss is taken as 1; callers scale the outputs themselves.
+ *
+ * The library allocates no device memory and never synchronises inside
+ * flce_fwd_bwd: all work is enqueued on the caller's stream and the caller
+ * owns every buffer, including the workspace.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtype of h, W and grad_h. */
+typedef enum { FLCE_DTYPE_BF16 = 0, FLCE_DTYPE_F32 = 1 } flce_dtype;
+
+/* Reduction of the per-row losses. */
+typedef enum { FLCE_REDUCTION_MEAN = 0, FLCE_REDUCTION_SUM = 1 } flce_reduction;
+
+/* Return codes. */
+enum {
+  FLCE_OK = 0,
+  FLCE_EINVAL = 1,        /* bad argument: null pointer, bad size, bad enum, misalignment */
+  FLCE_EWORKSPACE = 2,    /* workspace smaller than flce_workspace_size() for the call */
+  FLCE_EDEVICE = 3,       /* a HIP launch or runtime call failed */
+  FLCE_ELABEL = 4,        /* (device-detected) a label outside [0, V) that is not ignore_index */
+  FLCE_EUNSUPPORTED = 5   /* valid but unsupported shape, e.g. H not a multiple of 8 (bf16) / 4 (fp32) */
+};
+
+/*
+ * Chunk plan.  Tokens are processed in chunks of `chunk_rows` rows; one chunk's
+ * logits (padded to `vocab_padded` columns) is the largest transient, so the
+ * full [N, V] logits never exist ("chunked transients", DeepSeek-V3 page,
+ * Memory).  chunk_rows <= ceil(N / 2), hence at least two chunks for N >= 2.
+ */
+typedef struct {
+  int64_t chunk_rows;         /* C: tokens per chunk */
+  int64_t n_chunks;           /* ceil(N / C) (0 when N = 0) */
+  int64_t vocab_padded;       /* V rounded up to the 256-column tile */
+  int64_t split_k;            /* grad_h = G W is split over the vocabulary into this many parts */
+  size_t logits_chunk_bytes;  /* C * vocab_padded * sizeof(dtype) */
+  size_t workspace_bytes;     /* total workspace this plan needs */
+  size_t grad_W_bytes;        /* 4 * V * H: the caller's fp32 weight-gradient accumulator */
+} flce_plan_t;
+
+/*
+ * Compute the chunk plan for a call with these sizes that may use at most
+ * `budget_bytes` of workspace (0 = default budget of 16 GiB).  Pure host
+ * arithmetic; no GPU needed.  Returns FLCE_OK, FLCE_EINVAL (negative sizes,
+ * bad dtype, null `out`), FLCE_EUNSUPPORTED (H not a multiple of 8 for bf16 or
+ * 4 for fp32) or FLCE_EWORKSPACE (not even the smallest chunk fits).
+ */
+int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget_bytes, flce_plan_t* out);
+
+/*
+ * Workspace bytes needed by flce_fwd_bwd for these sizes under `budget_bytes`
+ * (0 = default budget).  Returns 0 if no plan exists (see flce_plan).  Passing
+ * exactly this many bytes to flce_fwd_bwd reproduces the same plan.
+ */
+size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t budget_bytes);
+
+/*
+ * Forward and backward of fused linear cross-entropy (see the top of this
+ * file for the formulas and sources).
+ *
+ * Arguments (all pointers are device pointers unless stated):
+ *   h          [N, H] row-major, dtype; 16-byte aligned.  Read only.
+ *   W          [V, H] row-major (nn.Linear weight layout), dtype; 16-byte aligned.  Read only.
+ *   labels     [N] int64; 8-byte aligned.  Read only.
+ *   N, H, V    N >= 0, H >= 1, V >= 1; H % 8 == 0 (bf16) or H % 4 == 0 (fp32).
+ *   ignore_index  rows with this label are excluded from the loss, from
+ *              n_correct and from the gradients.
+ *   softcap_T  logit softcap T; T <= 0 disables the cap.
+ *   multiplier output multiplier m, applied to the logits before the cap.
+ *   reduction  FLCE_REDUCTION_MEAN or FLCE_REDUCTION_SUM.
+ *   loss       [1] fp32, written.
+ *   grad_h     [N, H] dtype, written (gradient w.r.t. the caller's h); 16-byte aligned.
+ *   grad_W     [V, H] fp32, overwritten with this call's gradient; 16-byte aligned.
+ *   n_correct  [1] int64, written with the count of valid rows whose argmax is
+ *              the label; may be NULL.
+ *   stream     HIP stream on which every kernel is enqueued (0 = null stream).
+ *   dtype      FLCE_DTYPE_BF16 or FLCE_DTYPE_F32.
+ *   workspace  device scratch owned by the caller, 256-byte aligned, at least
+ *              flce_workspace_size(N, H, V, dtype, 0) bytes (or the size for the
+ *              budget the caller planned with).  Its contents on entry are
+ *              ignored; on return it holds the status word read by
+ *              flce_read_status.
+ *   workspace_bytes  size of `workspace`; the chunk plan is the largest that fits.
+ *
+ * Errors: argument checks run on the host before anything is enqueued; on
+ * FLCE_EINVAL / FLCE_EUNSUPPORTED / FLCE_EWORKSPACE no output is touched.
+ * FLCE_EDEVICE means a launch failed (outputs unspecified).  Labels outside
+ * [0, V) that are not ignore_index are detected on the device: outputs are
+ * then unspecified and flce_read_status returns FLCE_ELABEL.
+ * N = 0 or no valid row gives loss = 0, n_correct = 0 and zero gradients.
+ * Calls on distinct workspaces may run concurrently; two calls sharing a
+ * workspace must be ordered (same stream).
+ */
+int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels,
+                 int64_t N, int64_t H, int64_t V,
+                 int64_t ignore_index, float softcap_T, float multiplier, int reduction,
+                 float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
+                 hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes);
+
+/*
+ * Synchronise `stream` and return the device-side status of the last
+ * flce_fwd_bwd that used `workspace`: FLCE_OK or FLCE_ELABEL.  Returns
+ * FLCE_EINVAL for a null workspace and FLCE_EDEVICE if the copy fails.
+ */
+int flce_read_status(const void* workspace, hipStream_t stream);
+
+/* Static, human-readable text for a return code. */
+const char* flce_strerror(int code);
+
+/*
+ * Measurement facility (not part of the method): per-kernel timing with HIP
+ * events.  While enabled, every kernel that flce_fwd_bwd enqueues is
+ * bracketed by two events recorded on the same stream, so the elapsed time is
+ * that kernel's own duration on that stream.  Kinds index the arrays below.
+ */
+enum {
+  FLCE_KERNEL_LABEL_SCAN = 0,   /* header init + label scan (ignore mask, N_valid, range check) */
+  FLCE_KERNEL_FWD_LOGITS = 1,   /* logits GEMM + softcap / LSE / argmax / label-logit epilogue */
+  FLCE_KERNEL_ROW_MERGE = 2,    /* per-token log-sum-exp, loss, argmax */
+  FLCE_KERNEL_GRAD_LOGITS = 3,  /* softmax - onehot (x softcap derivative), in place */
+  FLCE_KERNEL_GRAD_H = 4,       /* grad_h GEMM G W (vocabulary-split partials) */
+  FLCE_KERNEL_GRAD_H_REDUCE = 5,/* sum of the partials, cast to the storage dtype */
+  FLCE_KERNEL_GRAD_W = 6,       /* grad_W GEMM G^T h, fp32 overwrite / read-modify-write */
+  FLCE_KERNEL_FINALIZE = 7,     /* loss scalar and n_correct */
+  FLCE_KERNEL_ZERO = 8,         /* zero grad_W when N = 0 */
+  FLCE_KERNEL_KINDS = 9
+};
+
+/* Turn event timing on (on != 0) or off for subsequent calls.  Returns FLCE_OK. */
+int flce_profile_enable(int on);
+
+/*
+ * Synchronise `stream`, fold all pending event pairs into the running totals
+ * and copy them out: total_ms[k] and launches[k] for k < FLCE_KERNEL_KINDS
+ * (caller-owned host arrays).  reset != 0 clears the totals afterwards.
+ * Returns FLCE_OK, FLCE_EINVAL (null array) or FLCE_EDEVICE.
+ */
+int flce_profile_read(hipStream_t stream, double* total_ms, int64_t* launches, int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

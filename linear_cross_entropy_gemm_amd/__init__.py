@@ -1,0 +1,34 @@
+"""MI355X-native fused linear cross-entropy (FLCE).
+
+The lm_head projection of hidden states onto the vocabulary, fused with the
+cross-entropy loss, the token-accuracy argmax and the backward pass, without
+ever materialising the [tokens, vocab] logits (Liger-Kernel "Muse Glimmer" and
+"DeepSeek-V3" commit pages, Summary and Memory sections).  All computation runs
+in the HIP kernels of ``libflce.so``; this package only marshals arguments and
+uses PyTorch for device memory and streams.
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    FLCE_DTYPE_BF16,
+    FLCE_DTYPE_F32,
+    FLCE_EDEVICE,
+    FLCE_EINVAL,
+    FLCE_ELABEL,
+    FLCE_EUNSUPPORTED,
+    FLCE_EWORKSPACE,
+    FLCE_OK,
+    FLCE_REDUCTION_MEAN,
+    FLCE_REDUCTION_SUM,
+    KERNEL_KINDS,
+    FlceError,
+    flce_fwd_bwd,
+    flce_profile_enable,
+    flce_profile_read,
+    flce_plan,
+    flce_read_status,
+    flce_strerror,
+    flce_workspace_size,
+)
+from .torch_api import FlceOutputs, fwd_bwd, linear_cross_entropy  # noqa: F401

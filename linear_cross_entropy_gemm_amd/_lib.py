@@ -1,0 +1,132 @@
+"""ctypes binding of ``libflce.so`` -- argument marshalling only.
+
+Each function here has the name and arguments of the C ABI declared in
+``include/flce.h``; every step of the computation runs in the library's HIP
+kernels.  Importing this module fails loudly when the library is missing: there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflce.so")
+
+FLCE_DTYPE_BF16 = 0
+FLCE_DTYPE_F32 = 1
+FLCE_REDUCTION_MEAN = 0
+FLCE_REDUCTION_SUM = 1
+
+FLCE_OK = 0
+FLCE_EINVAL = 1
+FLCE_EWORKSPACE = 2
+FLCE_EDEVICE = 3
+FLCE_ELABEL = 4
+FLCE_EUNSUPPORTED = 5
+
+# Every symbol include/flce.h declares.
+EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_read_status", "flce_strerror",
+            "flce_profile_enable", "flce_profile_read")
+
+# Kernel kinds of the per-kernel timing facility (index order of the arrays).
+KERNEL_KINDS = ("label_scan", "fwd_logits", "row_merge", "grad_logits", "grad_h", "grad_h_reduce",
+                "grad_W", "finalize", "zero")
+
+
+class flce_plan_t(ctypes.Structure):
+    _fields_ = [
+        ("chunk_rows", ctypes.c_int64),
+        ("n_chunks", ctypes.c_int64),
+        ("vocab_padded", ctypes.c_int64),
+        ("split_k", ctypes.c_int64),
+        ("logits_chunk_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("grad_W_bytes", ctypes.c_size_t),
+    ]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class FlceError(RuntimeError):
+    def __init__(self, code: int, where: str = ""):
+        self.code = code
+        super().__init__(f"{where}: FLCE error {code}: {flce_strerror(code)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python linear_cross_entropy_gemm_amd/build.py` "
+            "(the FLCE path has no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, sz, vp, i32, f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.flce_plan.argtypes = [i64, i64, i64, i32, sz, ctypes.POINTER(flce_plan_t)]
+    lib.flce_plan.restype = i32
+    lib.flce_workspace_size.argtypes = [i64, i64, i64, i32, sz]
+    lib.flce_workspace_size.restype = sz
+    lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
+                                 vp, vp, vp, vp, vp, i32, vp, sz]
+    lib.flce_fwd_bwd.restype = i32
+    lib.flce_read_status.argtypes = [vp, vp]
+    lib.flce_read_status.restype = i32
+    lib.flce_strerror.argtypes = [i32]
+    lib.flce_strerror.restype = ctypes.c_char_p
+    lib.flce_profile_enable.argtypes = [i32]
+    lib.flce_profile_enable.restype = i32
+    lib.flce_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), i32]
+    lib.flce_profile_read.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def flce_plan(N: int, H: int, V: int, dtype: int, budget_bytes: int = 0) -> flce_plan_t:
+    out = flce_plan_t()
+    rc = _lib.flce_plan(N, H, V, dtype, budget_bytes, ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_plan")
+    return out
+
+
+def flce_workspace_size(N: int, H: int, V: int, dtype: int, budget_bytes: int = 0) -> int:
+    return int(_lib.flce_workspace_size(N, H, V, dtype, budget_bytes))
+
+
+def flce_fwd_bwd(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_index: int,
+                 softcap_T: float, multiplier: float, reduction: int, loss: int, grad_h: int,
+                 grad_W: int, n_correct, stream: int, dtype: int, workspace: int,
+                 workspace_bytes: int) -> int:
+    """Raw call with device addresses as ints; returns the C return code."""
+    return int(_lib.flce_fwd_bwd(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier,
+                                 reduction, loss, grad_h, grad_W, n_correct, stream, dtype,
+                                 workspace, workspace_bytes))
+
+
+def flce_read_status(workspace: int, stream: int) -> int:
+    return int(_lib.flce_read_status(workspace, stream))
+
+
+def flce_strerror(code: int) -> str:
+    return _lib.flce_strerror(code).decode()
+
+
+def flce_profile_enable(on: bool) -> int:
+    return int(_lib.flce_profile_enable(1 if on else 0))
+
+
+def flce_profile_read(stream: int, reset: bool = True) -> dict:
+    """{kind: (total_ms, launches)} accumulated since the last reset."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    rc = _lib.flce_profile_read(stream, ms, cnt, 1 if reset else 0)
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_profile_read")
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def lib_handle() -> ctypes.CDLL:
+    return _lib

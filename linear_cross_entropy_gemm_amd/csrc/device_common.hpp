@@ -1,0 +1,80 @@
+// Device-side helpers shared by the FLCE kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Element traits: every K step moves 128 bytes of K per operand row, i.e. 8
+// chunks of 16 bytes; a chunk holds 8 bf16 or 4 fp32.
+template <typename T> struct Elem;
+template <> struct Elem<bf16> { static constexpr int size = 2; static constexpr int per_chunk = 8; };
+template <> struct Elem<float> { static constexpr int size = 4; static constexpr int per_chunk = 4; };
+
+__device__ __forceinline__ float fast_exp(float x) {
+  // e^x = 2^(x log2 e) on the hardware exp2 (v_exp_f32); exp(-inf) = 0.
+  return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// tanh for the logit softcap, written from the mathematics:
+//  * |x| < 0.25: the odd Maclaurin series x - x^3/3 + 2x^5/15 - 17x^7/315
+//    + 62x^9/2835 (the first omitted term is below 1e-8 relative there);
+//  * otherwise tanh|x| = 1 - 2 / (e^{2|x|} + 1), which saturates to 1 as
+//    e^{2|x|} overflows, with the sign restored.
+// Relative error is below 1e-6 over the whole range (tested against fp64).
+__host__ __device__ __forceinline__ float softcap_tanh(float x) {
+  const float x2 = x * x;
+  float p = 62.0f / 2835.0f;
+  p = p * x2 - 17.0f / 315.0f;
+  p = p * x2 + 2.0f / 15.0f;
+  p = p * x2 - 1.0f / 3.0f;
+  p = p * x2;
+  const float series = x + x * p;
+  const float ax = __builtin_fabsf(x);
+#if defined(__HIP_DEVICE_COMPILE__)
+  const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * ax);
+  const float r = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+#else
+  const float e = __builtin_exp2f(2.0f * kLog2e * ax);
+  const float r = 1.0f - 2.0f / (e + 1.0f);
+#endif
+  const float big = __builtin_copysignf(r, x);
+  return ax < 0.25f ? series : big;
+}
+
+// Online log-sum-exp / argmax state merge (running max m, sum of exp(z - m),
+// index of the first maximum).  Equal maxima keep the lower index.
+__device__ __forceinline__ void merge_stats(float& m, float& s, int& a, float m2, float s2, int a2) {
+  if (m2 == kNegInf) return;
+  if (m == kNegInf) { m = m2; s = s2; a = a2; return; }
+  const float M = __builtin_fmaxf(m, m2);
+  s = s * fast_exp(m - M) + s2 * fast_exp(m2 - M);
+  a = (m > m2) ? a : (m2 > m) ? a2 : (a < a2 ? a : a2);
+  m = M;
+}
+
+// Store 4 consecutive values as the storage dtype.
+__device__ __forceinline__ void store4(bf16* dst, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+  *reinterpret_cast<bf16x4*>(dst) = v;
+}
+__device__ __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+}  // namespace flce

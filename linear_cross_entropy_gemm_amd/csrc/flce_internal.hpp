@@ -1,0 +1,68 @@
+// Internal interfaces between the C ABI (flce_api.cpp), the chunk planner
+// (flce_plan.cpp) and the kernels (flce_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flce.h"
+
+namespace flce {
+
+// First 256 bytes of the workspace.
+struct Header {
+  int status;                  // FLCE_OK or FLCE_ELABEL, set on the device
+  int pad0;
+  unsigned long long n_valid;  // non-ignored rows of the call
+};
+
+constexpr size_t kHeaderBytes = 256;
+constexpr int64_t kVocabTile = 256;
+constexpr int64_t kRowTile = 256;
+
+// Chunk plan and workspace layout (byte offsets from the workspace base).
+struct Plan {
+  int64_t N, H, V, es;
+  int64_t C, n_chunks, Vp, nvt, split_k;
+  size_t off_lse, off_zlab, off_loss_row, off_pred;
+  size_t off_pmax, off_psum, off_parg;
+  size_t off_z, off_ghpart;
+  size_t total;
+};
+
+// Returns FLCE_OK and fills `out`, or an error code (no plan fits the budget).
+int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* out);
+
+struct CallArgs {
+  const void* h;
+  const void* W;
+  const int64_t* labels;
+  int64_t N, H, V, ignore_index;
+  float softcap_T, multiplier;
+  int reduction, dtype;
+  float* loss;
+  void* grad_h;
+  float* grad_W;
+  int64_t* n_correct;
+  void* workspace;
+};
+
+// Enqueue the whole call on `stream`.  Returns FLCE_OK or FLCE_EDEVICE.
+int run_call(const CallArgs& a, const Plan& pl, hipStream_t stream);
+
+// Brackets one kernel launch with timing events when profiling is enabled.
+class ProfileScope {
+ public:
+  ProfileScope(int kind, hipStream_t st);
+  ~ProfileScope();
+  ProfileScope(const ProfileScope&) = delete;
+  ProfileScope& operator=(const ProfileScope&) = delete;
+
+ private:
+  int kind_;
+  hipStream_t st_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+}  // namespace flce

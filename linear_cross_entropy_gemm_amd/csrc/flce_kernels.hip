@@ -1,0 +1,479 @@
+// HIP kernels of the fused linear cross-entropy path for gfx950, and the
+// per-call launch sequence.
+//
+// Per chunk of C tokens (Liger-Kernel DeepSeek-V3 page, Memory: chunked
+// transients instead of the [tokens, vocab] logits):
+//   fwd_logits     z = cap(m * h_c W^T) on MFMA, epilogue in registers: softcap,
+//                  per (token, 256-vocab tile) max / sum exp / first argmax,
+//                  the label's logit, z stored as the chunk's transient
+//   row_merge      per-token log-sum-exp, loss and argmax from the tile partials
+//   grad_logits    z -> G = m s (softmax - onehot) (1 - (z/T)^2), in place
+//   grad_h         partial[s] = G W over a slice of the vocabulary (MFMA)
+//   grad_h_reduce  grad_h rows = sum of the slices, cast to the storage dtype
+//   grad_W         grad_W (+)= G^T h_c (MFMA), fp32, overwrite on the first chunk
+// and once per call: header_init, label_scan (before), finalize (after).
+#include "kernel_args.hpp"
+#include "gemm_tile.hpp"
+
+namespace flce {
+
+// ---------------------------------------------------------------------------
+// Forward logit GEMM with the fused epilogue.  A = W rows (vocabulary on the
+// M side), B = h rows (tokens on the N side): each lane then owns one token
+// per 32 x 32 block and 16 of its vocabulary entries, so the row statistics
+// reduce in registers first, then across lanes l and l + 32, then across the
+// two waves that share the tokens.
+template <typename T>
+__device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn,
+                                             char* smem) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
+  const int vbase = tm * kTile + wm * 128 + hi * 4;
+  float best[4], sum[4];
+  int bidx[4];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn) {
+    const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
+    const bool tok_ok = tok < p.C_this;
+    const int64_t lab = tok_ok ? p.labels[tok] : INT64_MIN;
+    float mx = kNegInf;
+    int ax = 0x7fffffff;
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
+        float x = acc[bm][bn][v] * p.mult;
+        if (p.T > 0.0f) x = p.T * softcap_tanh(x * p.invT);
+        acc[bm][bn][v] = x;
+        // columns visit in increasing order: strict > keeps the first maximum
+        if (col < p.V && x > mx) {
+          mx = x;
+          ax = col;
+        }
+        if ((int64_t)col == lab) p.zlab[tok] = x;
+      }
+    }
+    if (tok_ok) {
+      T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + (int64_t)tok * p.ldz);
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store4(zr + vbase + bm * 32 + 8 * i, acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1],
+                 acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]);
+    }
+    float s = 0.0f;
+    if (mx != kNegInf) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
+          if (col < p.V) s += fast_exp(acc[bm][bn][v] - mx);
+        }
+    }
+    const float m2 = __shfl_xor(mx, 32);
+    const float s2 = __shfl_xor(s, 32);
+    const int a2 = __shfl_xor(ax, 32);
+    merge_stats(mx, s, ax, m2, s2, a2);  // lanes 0-31 carry the pair's result onwards
+    best[bn] = mx;
+    sum[bn] = s;
+    bidx[bn] = ax;
+  }
+  float* red_m = reinterpret_cast<float*>(smem);
+  float* red_s = red_m + 256;
+  int* red_a = reinterpret_cast<int*>(red_s + 256);
+  if (wm == 1 && hi == 0) {
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int idx = wn * 128 + bn * 32 + lo;
+      red_m[idx] = best[bn];
+      red_s[idx] = sum[bn];
+      red_a[idx] = bidx[bn];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && hi == 0) {
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int idx = wn * 128 + bn * 32 + lo;
+      const int tok = tn * kTile + idx;
+      if (tok < p.C_this) {
+        merge_stats(best[bn], sum[bn], bidx[bn], red_m[idx], red_s[idx], red_a[idx]);
+        const int64_t o = (int64_t)tm * p.ldp + tok;
+        p.pmax[o] = best[bn];
+        p.psum[o] = sum[bn];
+        p.parg[o] = bidx[bn];
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  int tm, tn, sp;
+  map_tile(p.map, tm, tn, sp);
+  const int64_t kbytes = (int64_t)p.H * Elem<T>::size;
+  KMajorLoader la, lb;
+  la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0);
+  lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0);
+  f32x16 acc[4][4];
+  const int nk = (int)((kbytes + kKBytes - 1) / kKBytes);
+  gemm_mainloop<T>(la, lb, nk, smem, acc);
+  fwd_epilogue<T>(acc, p, tm, tn, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Per-token merge of the vocabulary-tile partials: 64 tokens per block, 16
+// waves each merging every 16th tile, then a fixed-order merge of the waves.
+__global__ __launch_bounds__(1024) void row_merge_kernel(MergeArgs p) {
+  __shared__ float sm[16][64];
+  __shared__ float ss[16][64];
+  __shared__ int sa[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tok = blockIdx.x * 64 + lane;
+  float m = kNegInf, s = 0.0f;
+  int a = 0x7fffffff;
+  if (tok < p.C_this) {
+    for (int vt = w; vt < p.nvt; vt += 16) {
+      const int64_t o = (int64_t)vt * p.ldp + tok;
+      merge_stats(m, s, a, p.pmax[o], p.psum[o], p.parg[o]);
+    }
+  }
+  sm[w][lane] = m;
+  ss[w][lane] = s;
+  sa[w][lane] = a;
+  __syncthreads();
+  if (w == 0 && tok < p.C_this) {
+    for (int k = 1; k < 16; ++k) merge_stats(m, s, a, sm[k][lane], ss[k][lane], sa[k][lane]);
+    const float l = m + logf(s);
+    const int64_t lab = p.labels[tok];
+    p.lse[tok] = l;
+    p.pred[tok] = a;
+    p.loss_row[tok] = (lab != p.ignore_index) ? l - p.zlab[tok] : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// z -> G in place, 16 bytes per thread.  Padding columns (V <= v < Vp) and
+// ignored rows become exact zeros.
+template <typename T>
+__global__ __launch_bounds__(256) void grad_logits_kernel(GradLogitArgs p) {
+  constexpr int E = Elem<T>::per_chunk;
+  const int64_t vecs = p.Vp / E;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= vecs * p.C_this) return;
+  const int64_t row = idx / vecs;
+  const int col0 = (int)(idx - row * vecs) * E;
+  T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + row * p.ldz) + col0;
+  const int64_t lab = p.labels[row];
+  const bool valid = lab != p.ignore_index;
+  const unsigned long long nv = p.hdr->n_valid;
+  const float s = (p.reduction == FLCE_REDUCTION_MEAN) ? (nv ? 1.0f / (float)nv : 0.0f) : 1.0f;
+  const float scale = s * p.mult;
+  const float l = p.lse[row];
+  typedef T vec_t __attribute__((ext_vector_type(E)));
+  vec_t zv = *reinterpret_cast<const vec_t*>(zr);
+  vec_t gv;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int v = col0 + e;
+    const float z = to_f32(zv[e]);
+    float g = 0.0f;
+    if (valid && v < p.V) {
+      float d = fast_exp(z - l) - ((int64_t)v == lab ? 1.0f : 0.0f);
+      if (p.T > 0.0f) {
+        const float u = z * p.invT;
+        d *= 1.0f - u * u;
+      }
+      g = scale * d;
+    }
+    gv[e] = (T)g;
+  }
+  *reinterpret_cast<vec_t*>(zr) = gv;
+}
+
+// ---------------------------------------------------------------------------
+// grad_h partial over one vocabulary slice: rows = tokens (M), cols = hidden
+// (N), K = vocabulary.  A = G [C][Vp] (K contiguous), B = W [V][H] (N
+// contiguous, transposed through registers).
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  int tm, tn, sp;
+  map_tile(p.map, tm, tn, sp);
+  const int k0 = sp * p.ksteps_per_split;
+  const int rem = p.ksteps_total - k0;
+  const int nk = rem < p.ksteps_per_split ? rem : p.ksteps_per_split;
+  KMajorLoader la;
+  la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * Elem<T>::size, k0);
+  MNMajorLoader<T> lb;
+  lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0);
+  f32x16 acc[4][4];
+  gemm_mainloop<T>(la, lb, nk, smem, acc);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
+  float* out = p.part + (int64_t)sp * p.part_stride;
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int col = tn * kTile + wn * 128 + bn * 32 + lo;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = tm * kTile + wm * 128 + bm * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (row < p.C_this && col < p.H) out[(int64_t)row * p.H + col] = acc[bm][bn][v];
+      }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= p.n) return;
+  f32x4 a = *reinterpret_cast<const f32x4*>(p.part + i);
+  for (int s = 1; s < p.splits; ++s) a += *reinterpret_cast<const f32x4*>(p.part + s * p.part_stride + i);
+  store4(static_cast<T*>(p.out) + i, a[0], a[1], a[2], a[3]);
+}
+
+// ---------------------------------------------------------------------------
+// grad_W (+)= G^T h_c: rows = vocabulary (M), cols = hidden (N), K = tokens.
+// Both operands are stored with K as the slow dimension and are transposed
+// through registers.
+template <typename T>
+__global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  int tm, tn, sp;
+  map_tile(p.map, tm, tn, sp);
+  MNMajorLoader<T> la, lb;
+  la.init(p.G, p.ldg, tm * kTile, p.Vp, p.C_this, 0);
+  lb.init(p.h, p.ldh, tn * kTile, p.H, p.C_this, 0);
+  constexpr int bk = kKBytes / Elem<T>::size;
+  const int nk = (p.C_this + bk - 1) / bk;
+  f32x16 acc[4][4];
+  gemm_mainloop<T>(la, lb, nk, smem, acc);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+      const int col = tn * kTile + wn * 128 + bn * 32 + lo;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = tm * kTile + wm * 128 + bm * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        if (row < p.V && col < p.H) {
+          float* dst = p.gW + (int64_t)row * p.H + col;
+          float val = acc[bm][bn][v];
+          if (p.accumulate) val += *dst;
+          *dst = val;
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+__global__ void header_init_kernel(Header* hdr) {
+  if (threadIdx.x == 0) {
+    hdr->status = FLCE_OK;
+    hdr->n_valid = 0ull;
+  }
+}
+
+__global__ __launch_bounds__(256) void label_scan_kernel(const int64_t* labels, int64_t N, int64_t V,
+                                                         int64_t ignore_index, Header* hdr) {
+  __shared__ unsigned long long cnt[256];
+  __shared__ int bad[256];
+  unsigned long long c = 0;
+  int b = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 256) {
+    const int64_t l = labels[i];
+    if (l != ignore_index) {
+      ++c;
+      if (l < 0 || l >= V) b = 1;
+    }
+  }
+  cnt[threadIdx.x] = c;
+  bad[threadIdx.x] = b;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      cnt[threadIdx.x] += cnt[threadIdx.x + s];
+      bad[threadIdx.x] |= bad[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (cnt[0]) atomicAdd(&hdr->n_valid, cnt[0]);
+    if (bad[0]) atomicOr(&hdr->status, FLCE_ELABEL);
+  }
+}
+
+// loss = s * sum of the per-row losses (fp64, fixed order), n_correct.
+__global__ __launch_bounds__(1024) void finalize_kernel(FinalizeArgs p) {
+  __shared__ double ls[1024];
+  __shared__ long long cs[1024];
+  double a = 0.0;
+  long long c = 0;
+  for (int64_t i = threadIdx.x; i < p.N; i += 1024) {
+    const int64_t lab = p.labels[i];
+    if (lab != p.ignore_index) {
+      a += (double)p.loss_row[i];
+      c += (p.pred[i] == lab) ? 1 : 0;
+    }
+  }
+  ls[threadIdx.x] = a;
+  cs[threadIdx.x] = c;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      ls[threadIdx.x] += ls[threadIdx.x + s];
+      cs[threadIdx.x] += cs[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const unsigned long long nv = p.hdr->n_valid;
+    const double s = (p.reduction == FLCE_REDUCTION_MEAN) ? (nv ? 1.0 / (double)nv : 0.0) : 1.0;
+    *p.loss = (float)(s * ls[0]);
+    if (p.n_correct) *p.n_correct = cs[0];
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Launch sequence.
+static inline unsigned grid_1d(int64_t work, int64_t per_block) {
+  return (unsigned)((work + per_block - 1) / per_block);
+}
+
+template <typename T>
+static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
+  constexpr int es = Elem<T>::size;
+  char* ws = static_cast<char*>(a.workspace);
+  Header* hdr = reinterpret_cast<Header*>(ws);
+  float* lse = reinterpret_cast<float*>(ws + pl.off_lse);
+  float* zlab = reinterpret_cast<float*>(ws + pl.off_zlab);
+  float* loss_row = reinterpret_cast<float*>(ws + pl.off_loss_row);
+  int* pred = reinterpret_cast<int*>(ws + pl.off_pred);
+  float* pmax = reinterpret_cast<float*>(ws + pl.off_pmax);
+  float* psum = reinterpret_cast<float*>(ws + pl.off_psum);
+  int* parg = reinterpret_cast<int*>(ws + pl.off_parg);
+  void* zbuf = ws + pl.off_z;
+  float* ghpart = reinterpret_cast<float*>(ws + pl.off_ghpart);
+
+  const int H = (int)a.H, V = (int)a.V, Vp = (int)pl.Vp;
+  const int C = (int)pl.C;
+  const float invT = a.softcap_T > 0.0f ? 1.0f / a.softcap_T : 0.0f;
+  const float capT = a.softcap_T > 0.0f ? a.softcap_T : 0.0f;
+
+  {
+    ProfileScope ps(FLCE_KERNEL_LABEL_SCAN, st);
+    header_init_kernel<<<1, 64, 0, st>>>(hdr);
+    if (a.N > 0) {
+      const unsigned g = grid_1d(a.N, 256);
+      label_scan_kernel<<<g < 1024 ? g : 1024, 256, 0, st>>>(a.labels, a.N, a.V, a.ignore_index, hdr);
+    }
+  }
+  if (pl.n_chunks == 0) {
+    ProfileScope ps(FLCE_KERNEL_ZERO, st);
+    const int64_t n = a.V * a.H;
+    const unsigned g = grid_1d(n, 256);
+    zero_f32_kernel<<<g < 65536 ? g : 65536, 256, 0, st>>>(a.grad_W, n);
+  }
+  for (int64_t ck = 0; ck < pl.n_chunks; ++ck) {
+    const int64_t c0 = ck * pl.C;
+    const int Ct = (int)((a.N - c0) < pl.C ? (a.N - c0) : pl.C);
+    const char* hc = static_cast<const char*>(a.h) + c0 * a.H * es;
+    const int64_t* lc = a.labels + c0;
+    const int tiles_tok = (Ct + kTile - 1) / kTile;
+    const int tiles_voc = Vp / kTile;
+    const int tiles_hid = (H + kTile - 1) / kTile;
+
+    FwdArgs f;
+    f.h = hc; f.W = a.W; f.labels = lc;
+    f.ldh = a.H * es; f.ldw = a.H * es;
+    f.C_this = Ct; f.H = H; f.V = V; f.Vp = Vp;
+    f.mult = a.multiplier; f.T = capT; f.invT = invT;
+    f.z = zbuf; f.ldz = (int64_t)Vp * es;
+    f.pmax = pmax; f.psum = psum; f.parg = parg; f.ldp = C;
+    f.zlab = zlab + c0;
+    f.map = TileMap{tiles_voc, tiles_tok, 1, 1, 0};
+    {
+      ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
+      fwd_logits_kernel<T><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(f);
+    }
+
+    MergeArgs m;
+    m.pmax = pmax; m.psum = psum; m.parg = parg; m.ldp = C; m.nvt = tiles_voc;
+    m.labels = lc; m.ignore_index = a.ignore_index;
+    m.zlab = zlab + c0; m.lse = lse + c0; m.loss_row = loss_row + c0; m.pred = pred + c0;
+    m.C_this = Ct;
+    {
+      ProfileScope ps(FLCE_KERNEL_ROW_MERGE, st);
+      row_merge_kernel<<<grid_1d(Ct, 64), 1024, 0, st>>>(m);
+    }
+
+    GradLogitArgs gl;
+    gl.z = zbuf; gl.ldz = (int64_t)Vp * es; gl.C_this = Ct; gl.V = V; gl.Vp = Vp;
+    gl.labels = lc; gl.ignore_index = a.ignore_index; gl.lse = lse + c0; gl.hdr = hdr;
+    gl.reduction = a.reduction; gl.mult = a.multiplier; gl.T = capT; gl.invT = invT;
+    {
+      ProfileScope ps(FLCE_KERNEL_GRAD_LOGITS, st);
+      grad_logits_kernel<T><<<grid_1d((int64_t)Ct * (Vp / Elem<T>::per_chunk), 256), 256, 0, st>>>(gl);
+    }
+
+    GradHArgs gh;
+    gh.G = zbuf; gh.ldg = (int64_t)Vp * es; gh.W = a.W; gh.ldw = a.H * es;
+    gh.C_this = Ct; gh.H = H; gh.V = V; gh.Vp = Vp;
+    gh.ksteps_total = (int)(((int64_t)Vp * es) / kKBytes);
+    gh.ksteps_per_split = (gh.ksteps_total + (int)pl.split_k - 1) / (int)pl.split_k;
+    const int splits = (gh.ksteps_total + gh.ksteps_per_split - 1) / gh.ksteps_per_split;
+    gh.part = ghpart; gh.part_stride = (int64_t)C * H;
+    gh.map = TileMap{tiles_tok, tiles_hid, splits, tiles_tok, 0};
+    {
+      ProfileScope ps(FLCE_KERNEL_GRAD_H, st);
+      grad_h_kernel<T><<<tiles_tok * tiles_hid * splits, kThreads, 0, st>>>(gh);
+    }
+
+    GradHReduceArgs gr;
+    gr.part = ghpart; gr.part_stride = (int64_t)C * H; gr.splits = splits;
+    gr.n = (int64_t)Ct * H;
+    gr.out = static_cast<char*>(a.grad_h) + c0 * a.H * es;
+    {
+      ProfileScope ps(FLCE_KERNEL_GRAD_H_REDUCE, st);
+      grad_h_reduce_kernel<T><<<grid_1d(gr.n / 4, 256), 256, 0, st>>>(gr);
+    }
+
+    GradWArgs gw;
+    gw.G = zbuf; gw.ldg = (int64_t)Vp * es; gw.h = hc; gw.ldh = a.H * es;
+    gw.C_this = Ct; gw.H = H; gw.V = V; gw.Vp = Vp;
+    gw.gW = a.grad_W; gw.accumulate = ck > 0 ? 1 : 0;
+    gw.map = TileMap{tiles_voc, tiles_hid, 1, 4, 1};
+    {
+      ProfileScope ps(FLCE_KERNEL_GRAD_W, st);
+      grad_W_kernel<T><<<tiles_voc * tiles_hid, kThreads, 0, st>>>(gw);
+    }
+  }
+  FinalizeArgs fa;
+  fa.labels = a.labels; fa.N = a.N; fa.ignore_index = a.ignore_index;
+  fa.loss_row = loss_row; fa.pred = pred; fa.hdr = hdr; fa.reduction = a.reduction;
+  fa.loss = a.loss; fa.n_correct = a.n_correct;
+  {
+    ProfileScope ps(FLCE_KERNEL_FINALIZE, st);
+    finalize_kernel<<<1, 1024, 0, st>>>(fa);
+  }
+  return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_EDEVICE;
+}
+
+int run_call(const CallArgs& a, const Plan& pl, hipStream_t stream) {
+  if (a.dtype == FLCE_DTYPE_BF16) return run_typed<bf16>(a, pl, stream);
+  return run_typed<float>(a, pl, stream);
+}
+
+}  // namespace flce

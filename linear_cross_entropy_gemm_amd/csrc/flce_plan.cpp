@@ -1,0 +1,126 @@
+// Chunk planner: chooses the token chunk C and lays out the workspace.
+//
+// The chunk's logits [C, Vp] are the largest transient ("chunked transients"
+// in place of the [tokens, vocab] logits, Liger-Kernel DeepSeek-V3 page,
+// Memory).  C is the largest multiple of the 256-row tile with
+// C <= ceil(N / 2) whose workspace fits the budget, so every call with N >= 2
+// runs at least two chunks and the full logits never exist.  With 288 GB of
+// HBM per MI355X the default 16 GiB budget never binds for the lm_head shapes
+// of the pages (Muse Glimmer 6656 x 202048, DeepSeek-V3 7168 x 129280).
+#include <algorithm>
+
+#include "flce_internal.hpp"
+
+namespace flce {
+
+namespace {
+
+constexpr size_t kDefaultBudget = size_t(16) << 30;
+constexpr int64_t kCUs = 256;       // MI355X compute units (one 256x256 tile each)
+constexpr int64_t kMinSplitSteps = 64;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// grad_h = G W has K = vocabulary, long and narrow output: split K so that the
+// number of tiles fills whole waves of the 256 CUs.  Picks the split with the
+// best wave efficiency (smallest on ties) among those leaving >= 64 K steps
+// per split.
+int64_t choose_split(int64_t C, int64_t H, int64_t Vp, int64_t es) {
+  const int64_t tiles = ((C + kRowTile - 1) / kRowTile) * ((H + 255) / 256);
+  const int64_t ksteps = Vp * es / 128;
+  int64_t best_s = 1;
+  double best_eff = 0.0;
+  for (int64_t s = 1; s <= 16; ++s) {
+    if (s > 1 && ksteps / s < kMinSplitSteps) break;
+    const int64_t per = (ksteps + s - 1) / s;
+    const int64_t real = (ksteps + per - 1) / per;
+    const int64_t work = tiles * real;
+    const int64_t waves = (work + kCUs - 1) / kCUs;
+    const double eff = double(work) / double(waves * kCUs);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best_s = real;
+    }
+  }
+  return best_s;
+}
+
+void layout(Plan* p) {
+  size_t off = kHeaderBytes;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t N = size_t(p->N);
+  p->off_lse = take(N * 4);
+  p->off_zlab = take(N * 4);
+  p->off_loss_row = take(N * 4);
+  p->off_pred = take(N * 4);
+  const size_t part = size_t(p->nvt) * size_t(p->C) * 4;
+  p->off_pmax = take(part);
+  p->off_psum = take(part);
+  p->off_parg = take(part);
+  p->off_z = take(size_t(p->C) * size_t(p->Vp) * size_t(p->es));
+  p->off_ghpart = take(size_t(p->split_k) * size_t(p->C) * size_t(p->H) * 4);
+  p->total = off;
+}
+
+}  // namespace
+
+int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* out) {
+  if (!out) return FLCE_EINVAL;
+  if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
+  if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
+  const int64_t es = dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  if ((H * es) % 16 != 0) return FLCE_EUNSUPPORTED;
+  // 32-bit indices inside the kernels
+  if (N > (int64_t(1) << 31) - 1 || H > (int64_t(1) << 24) || V > (int64_t(1) << 30))
+    return FLCE_EUNSUPPORTED;
+  if (budget == 0) budget = kDefaultBudget;
+
+  Plan p{};
+  p.N = N;
+  p.H = H;
+  p.V = V;
+  p.es = es;
+  p.Vp = (V + kVocabTile - 1) / kVocabTile * kVocabTile;
+  p.nvt = p.Vp / kVocabTile;
+  if (N == 0) {
+    p.C = 0;
+    p.n_chunks = 0;
+    p.split_k = 1;
+    layout(&p);
+    if (p.total > budget) return FLCE_EWORKSPACE;
+    *out = p;
+    return FLCE_OK;
+  }
+  const int64_t half = (N + 1) / 2;
+  int64_t c = half < kRowTile ? half : half / kRowTile * kRowTile;
+  for (;;) {
+    p.C = c;
+    p.n_chunks = (N + c - 1) / c;
+    p.split_k = choose_split(c, H, p.Vp, es);
+    layout(&p);
+    if (p.total <= budget) {
+      *out = p;
+      return FLCE_OK;
+    }
+    if (c <= kRowTile) break;
+    c -= kRowTile;
+  }
+  // below one row tile: halve until it fits
+  for (c = std::min<int64_t>(c, kRowTile) / 2; c >= 1; c /= 2) {
+    p.C = c;
+    p.n_chunks = (N + c - 1) / c;
+    p.split_k = choose_split(c, H, p.Vp, es);
+    layout(&p);
+    if (p.total <= budget) {
+      *out = p;
+      return FLCE_OK;
+    }
+  }
+  return FLCE_EWORKSPACE;
+}
+
+}  // namespace flce

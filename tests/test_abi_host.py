@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, plans chunks as documented and rejects bad arguments before touching
+the GPU (no compute call runs here)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = pytest.importorskip("linear_cross_entropy_gemm_amd")
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "flce.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    decl = declared_symbols()
+    assert decl == sorted(L.EXPORTED)
+    lib = ctypes.CDLL(L._lib.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_strerror():
+    for code in range(6):
+        assert L.flce_strerror(code) and L.flce_strerror(code) != "unknown error code"
+    assert L.flce_strerror(99) == "unknown error code"
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_plan_invariants(name):
+    c = synth.CONFIGS[name]
+    dt = L.FLCE_DTYPE_BF16 if c.dtype == "bf16" else L.FLCE_DTYPE_F32
+    es = 2 if c.dtype == "bf16" else 4
+    p = L.flce_plan(c.N, c.H, c.V, dt)
+    half = (c.N + 1) // 2
+    assert p.chunk_rows <= half and p.n_chunks >= 2
+    assert p.chunk_rows % 256 == 0 or p.chunk_rows == half
+    assert p.n_chunks == -(-c.N // p.chunk_rows)
+    assert p.vocab_padded % 256 == 0 and p.vocab_padded - 256 < c.V <= p.vocab_padded
+    assert p.logits_chunk_bytes == p.chunk_rows * p.vocab_padded * es
+    # the transient never reaches the size of the full [N, V] logits
+    assert p.logits_chunk_bytes < c.N * c.V * es
+    assert p.grad_W_bytes == 4 * c.V * c.H
+    assert L.flce_workspace_size(c.N, c.H, c.V, dt) == p.workspace_bytes
+    # planning again with exactly that many bytes reproduces the plan
+    q = L.flce_plan(c.N, c.H, c.V, dt, p.workspace_bytes)
+    assert q.as_dict() == p.as_dict()
+
+
+def test_plan_budget_shrinks_chunks():
+    c = synth.CONFIGS["c4"]
+    full = L.flce_plan(c.N, c.H, c.V, 0)
+    small = L.flce_plan(c.N, c.H, c.V, 0, full.workspace_bytes // 3)
+    assert small.chunk_rows < full.chunk_rows and small.workspace_bytes <= full.workspace_bytes // 3
+    with pytest.raises(L.FlceError) as e:
+        L.flce_plan(c.N, c.H, c.V, 0, 1 << 16)
+    assert e.value.code == L.FLCE_EWORKSPACE
+
+
+def test_plan_small_and_degenerate():
+    p = L.flce_plan(1, 8, 5, 0)
+    assert (p.chunk_rows, p.n_chunks) == (1, 1)
+    p = L.flce_plan(0, 8, 5, 0)
+    assert (p.chunk_rows, p.n_chunks) == (0, 0)
+    p = L.flce_plan(600, 320, 1000, 0)
+    assert (p.chunk_rows, p.n_chunks) == (256, 3)
+    p = L.flce_plan(300, 64, 100, 1)
+    assert (p.chunk_rows, p.n_chunks) == (150, 2)
+
+
+def test_plan_rejects():
+    for args, code in [((-1, 8, 8, 0), L.FLCE_EINVAL), ((4, 0, 8, 0), L.FLCE_EINVAL),
+                       ((4, 8, 0, 0), L.FLCE_EINVAL), ((4, 8, 8, 7), L.FLCE_EINVAL),
+                       ((4, 12, 8, 0), L.FLCE_EUNSUPPORTED), ((4, 6, 8, 1), L.FLCE_EUNSUPPORTED)]:
+        with pytest.raises(L.FlceError) as e:
+            L.flce_plan(*args)
+        assert e.value.code == code, args
+        assert L.flce_workspace_size(*args) == 0
+
+
+def test_accumulator_sizes_match_the_pages():
+    """The fp32 [vocab, hidden] accumulator the plan reports equals the sizes
+    the pages print (tests/golden/pages_sizes.json)."""
+    fx = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_sizes.json")))
+    for a in fx["accumulators"]:
+        p = L.flce_plan(4096, a["hidden"], a["vocab"], 0)
+        b = p.grad_W_bytes if a["dtype"] == "fp32" else p.grad_W_bytes // 2
+        if a.get("unit") == "GiB":
+            b = b / 2**30
+        assert a["bytes_lo"] <= b <= a["bytes_hi"], a
+
+
+def _call(**kw):
+    args = dict(h=16, W=16, labels=8, N=4, H=8, V=8, ignore_index=-100, softcap_T=0.0,
+                multiplier=1.0, reduction=0, loss=4, grad_h=16, grad_W=16, n_correct=None,
+                stream=0, dtype=0, workspace=256, workspace_bytes=64)
+    args.update(kw)
+    return L.flce_fwd_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), L.FLCE_EINVAL),
+    (dict(reduction=2), L.FLCE_EINVAL),
+    (dict(N=-1), L.FLCE_EINVAL),
+    (dict(H=0), L.FLCE_EINVAL),
+    (dict(V=0), L.FLCE_EINVAL),
+    (dict(W=None), L.FLCE_EINVAL),
+    (dict(grad_W=None), L.FLCE_EINVAL),
+    (dict(loss=None), L.FLCE_EINVAL),
+    (dict(workspace=None), L.FLCE_EINVAL),
+    (dict(h=None), L.FLCE_EINVAL),
+    (dict(labels=None), L.FLCE_EINVAL),
+    (dict(grad_h=None), L.FLCE_EINVAL),
+    (dict(h=24), L.FLCE_EINVAL),          # misaligned
+    (dict(W=8), L.FLCE_EINVAL),
+    (dict(workspace=512 + 16), L.FLCE_EINVAL),
+    (dict(labels=12), L.FLCE_EINVAL),
+    (dict(softcap_T=float("nan")), L.FLCE_EINVAL),
+    (dict(softcap_T=float("inf")), L.FLCE_EINVAL),
+    (dict(multiplier=float("inf")), L.FLCE_EINVAL),
+    (dict(H=12), L.FLCE_EUNSUPPORTED),
+    (dict(), L.FLCE_EWORKSPACE),
+])
+def test_fwd_bwd_rejects_before_launch(kw, code):
+    # Every pointer here is a fake address.  The base arguments already fail
+    # the workspace check (64 bytes), so no variant can reach a launch; each
+    # variant must be rejected by its own, earlier check.
+    assert _call(**kw) == code
+
+
+def test_read_status_null():
+    assert L.flce_read_status(None, 0) == L.FLCE_EINVAL

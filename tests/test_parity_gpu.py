@@ -1,0 +1,183 @@
+"""GPU parity against the full fp64 oracle, element by element, at shapes the
+oracle finishes in seconds that still span several 256-wide tiles, several
+token chunks and ragged tails; plus edge cases and determinism.
+
+Tolerances (relative loss error / relative Frobenius error of each gradient):
+fp32 1e-5 / 1e-4, bf16 2e-3 / 2e-2.  n_correct must fall in the window of
+``oracle.n_correct_window`` (exact on rows whose top-2 margin exceeds 1e-2).
+Ignored rows must have exactly zero grad_h.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import log, rel_fro, run_case, to_device, tolerances
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("require_gpu")]
+
+IGN = synth.IGNORE_INDEX
+
+# (id, base, N, H, V, T, m, reduction)
+CASES = [
+    ("c1", "c1", None, None, None, None, None, None),
+    ("bf16_ragged_T1", "c2", 600, 320, 1000, 1.0, 0.37, "mean"),
+    ("bf16_ragged_T2_sum", "c4", 520, 256, 777, 2.0, 0.5, "sum"),
+    ("bf16_zipf_nocap", "c3", 700, 384, 1500, 0.0, 1.0, "mean"),
+    ("bf16_T30_m05", "c4", 513, 448, 2100, 30.0, 0.5, "mean"),
+    ("f32_T1", "c1", 300, 96, 530, 1.0, 0.5, "mean"),
+    ("f32_nocap_sum", "c1", 257, 64, 2000, 0.0, 1.0, "sum"),
+    ("bf16_tail_pad_sum", "c5", 1024, 128, 1300, 30.0, 1.0, "sum"),
+    ("bf16_tiny_vocab", "c2", 90, 64, 37, 1.0, 1.0, "mean"),
+    ("bf16_H8", "c2", 300, 8, 300, 0.0, 1.0, "mean"),
+    ("f32_H4", "c1", 130, 4, 260, 2.0, 1.0, "mean"),
+    ("bf16_one_row", "c2", 1, 64, 300, 0.0, 1.0, "mean"),
+]
+
+
+def make(base, N, H, V, T, m, red, seed=None, ignore_frac=None):
+    kw = {}
+    if T is not None:
+        kw.update(softcap_T=T, multiplier=m, reduction=red)
+    if ignore_frac is not None:
+        kw["ignore_frac"] = ignore_frac
+    if N is not None and synth.CONFIGS[base].seq_len:
+        kw["seq_len"] = max(1, N // 4)
+    cfg = synth.small_config(base, **kw)
+    return synth.make_case(cfg, N=N, H=H, V=V, seed=seed)
+
+
+def reference(case):
+    c = case.cfg
+    return oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, IGN, c.softcap_T,
+                                 c.multiplier, c.reduction)
+
+
+def check(case, o, ref):
+    lt, gt = tolerances(case.cfg.dtype)
+    loss = float(o.loss.item())
+    gh = o.grad_h.float().cpu().numpy()
+    gW = o.grad_W.cpu().numpy()
+    nc = int(o.n_correct.item())
+    e_loss = abs(loss - ref["loss"]) / max(abs(ref["loss"]), 1e-30)
+    e_gh = rel_fro(gh, ref["grad_h"])
+    e_gW = rel_fro(gW, ref["grad_W"])
+    lo, hi = oracle.n_correct_window(ref["pred"], ref["margin"], ref["z_label"], ref["M"],
+                                     case.labels, ref["valid"])
+    log(f"  loss {loss:.8g} ref {ref['loss']:.8g} rel {e_loss:.2e} | grad_h {e_gh:.2e} "
+        f"grad_W {e_gW:.2e} | n_correct {nc} in [{lo},{hi}]")
+    assert e_loss <= lt
+    assert e_gh <= gt
+    assert e_gW <= gt
+    assert lo <= nc <= hi
+    ign = case.labels == IGN
+    assert np.all(gh[ign] == 0.0)
+
+
+@pytest.mark.parametrize("cid,base,N,H,V,T,m,red", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(cid, base, N, H, V, T, m, red):
+    case = make(base, N, H, V, T, m, red)
+    c = case.cfg
+    log(f"[parity] {cid}: {c.dtype} N={c.N} H={c.H} V={c.V} T={c.softcap_T} m={c.multiplier} {c.reduction}")
+    ref = reference(case)
+    o = run_case(case)
+    check(case, o, ref)
+
+
+@pytest.mark.parametrize("dtype_base", ["c2", "c1"])
+def test_planted_labels_count_exactly(dtype_base):
+    """Half of the valid rows get their own argmax as label, so n_correct is
+    large and known."""
+    case = make(dtype_base, 640, 128, 900, 0.0, 1.0, "mean", seed=77)
+    log(f"[planted] {case.cfg.dtype}")
+    ref = reference(case)
+    rng = np.random.default_rng(5)
+    valid = case.labels != IGN
+    plant = valid & (rng.random(case.cfg.N) < 0.5)
+    case.labels[plant] = ref["pred"][plant]
+    ref = reference(case)
+    o = run_case(case)
+    check(case, o, ref)
+    assert int(o.n_correct.item()) >= int(0.4 * plant.sum())
+
+
+@pytest.mark.parametrize("base", ["c2", "c1"])
+def test_all_rows_ignored(base):
+    case = make(base, 300, 64, 500, 1.0, 0.5, "mean")
+    case.labels[:] = IGN
+    log(f"[all-ignored] {case.cfg.dtype}")
+    o = run_case(case)
+    assert float(o.loss.item()) == 0.0 and int(o.n_correct.item()) == 0
+    assert not o.grad_h.float().abs().max().item()
+    assert not o.grad_W.abs().max().item()
+
+
+def test_empty_batch():
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    log("[empty]")
+    dev = torch.device("cuda", 0)
+    h = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    W = torch.randn((300, 64), device=dev).to(torch.bfloat16)
+    lab = torch.zeros((0,), dtype=torch.int64, device=dev)
+    o = L.fwd_bwd(h, W, lab)
+    torch.cuda.synchronize()
+    assert float(o.loss.item()) == 0.0 and int(o.n_correct.item()) == 0
+    assert o.grad_W.abs().max().item() == 0.0
+
+
+def test_other_ignore_index():
+    """A vocabulary id used as ignore_index excludes exactly those rows."""
+    import linear_cross_entropy_gemm_amd as L
+    import torch
+    case = make("c2", 400, 64, 50, 0.0, 1.0, "mean", ignore_frac=0.0)
+    log("[ignore_index=3]")
+    ref = oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, 3, 0.0, 1.0, "mean")
+    h, W, lab = to_device(case)
+    o = L.fwd_bwd(h, W, lab, ignore_index=3)
+    torch.cuda.synchronize()
+    ok = case.labels != 3
+    assert abs(float(o.loss.item()) - ref["loss"]) / ref["loss"] <= 2e-3
+    assert rel_fro(o.grad_W.cpu().numpy(), ref["grad_W"]) <= 2e-2
+    assert np.all(o.grad_h.float().cpu().numpy()[~ok] == 0.0)
+
+
+def test_bad_label_sets_status():
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c2", 200, 64, 300, 0.0, 1.0, "mean")
+    case.labels[17] = 300          # == V, out of range
+    case.labels[18] = -3
+    log("[bad-label]")
+    h, W, lab = to_device(case)
+    with pytest.raises(L.FlceError) as e:
+        L.fwd_bwd(h, W, lab)
+    assert e.value.code == L.FLCE_ELABEL
+
+
+def test_deterministic():
+    case = make("c4", 700, 256, 1100, 30.0, 0.5, "mean")
+    log("[determinism]")
+    h, W, lab = to_device(case)
+    a = run_case(case, h, W, lab)
+    a = (a.loss.clone(), a.grad_h.clone(), a.grad_W.clone(), a.n_correct.clone())
+    b = run_case(case, h, W, lab)
+    assert a[0].item() == b.loss.item() and a[3].item() == b.n_correct.item()
+    import torch
+    assert torch.equal(a[1], b.grad_h) and torch.equal(a[2], b.grad_W)
+
+
+def test_autograd_wrapper_scales_by_upstream_gradient():
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c1", 200, 32, 300, 1.0, 0.7, "mean")
+    log("[autograd]")
+    ref = reference(case)
+    h, W, lab = to_device(case)
+    h.requires_grad_(True)
+    W.requires_grad_(True)
+    loss, nc = L.linear_cross_entropy(h, W, lab, softcap=1.0, multiplier=0.7)
+    (3.0 * loss).backward()
+    torch.cuda.synchronize()
+    assert abs(loss.item() - ref["loss"]) / ref["loss"] <= 1e-5
+    assert rel_fro(h.grad.cpu().numpy(), 3.0 * ref["grad_h"]) <= 1e-4
+    assert rel_fro(W.grad.cpu().numpy(), 3.0 * ref["grad_W"]) <= 1e-4
