@@ -1,0 +1,89 @@
+"""GPU parity at the full lm_head sizes, in the launch configuration bench.py
+times (default chunk plan).
+
+Per workload (c2..c5 of ``synth.CONFIGS``):
+* loss against the fp64 oracle's reduced loss stored by
+  ``tests/golden/make_rowstats.py`` (relative error <= 2e-3);
+* n_correct inside the oracle's window (exact on rows whose top-2 margin
+  exceeds 1e-2);
+* grad_h on 64 seeded valid rows and grad_W on 64 seeded + 64 label-drawn
+  vocabulary rows, recomputed by the oracle on the spot (relative Frobenius
+  error <= 2e-2);
+* at every entry: grad_h of ignored rows is exactly zero; without a softcap
+  every column of grad_W sums to zero up to the first-order effect of the
+  bf16 logit/gradient transients.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import log, rel_fro, run_case, to_device
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("require_gpu")]
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+IGN = synth.IGNORE_INDEX
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size(name):
+    import torch
+    cfg = synth.CONFIGS[name]
+    gold = np.load(os.path.join(GOLDEN, f"{name}_rowstats.npz"))
+    log(f"[full] {name}: N={cfg.N} H={cfg.H} V={cfg.V} T={cfg.softcap_T} m={cfg.multiplier} {cfg.reduction}")
+    case = synth.make_case(cfg)
+    assert case.digest() == str(gold["digest"]), "seeded inputs differ from the stored oracle run"
+    h, W, lab = to_device(case)
+    o = run_case(case, h, W, lab)
+    log(f"[full] {name}: GPU done, loss {o.loss.item():.8g} oracle {float(gold['loss']):.8g}")
+
+    ref_loss = float(gold["loss"])
+    assert abs(o.loss.item() - ref_loss) / abs(ref_loss) <= 2e-3
+
+    valid = case.labels != IGN
+    lo, hi = oracle.n_correct_window(gold["pred"], gold["margin"], gold["z_label"], gold["M"],
+                                     case.labels, valid)
+    nc = int(o.n_correct.item())
+    log(f"[full] {name}: n_correct {nc} in [{lo}, {hi}]")
+    assert lo <= nc <= hi
+
+    ign = torch.from_numpy(np.nonzero(~valid)[0]).to(h.device)
+    if len(ign):
+        assert o.grad_h.index_select(0, ign).abs().max().item() == 0.0
+
+    n_valid = int(valid.sum())
+    s = oracle.reduction_scale(n_valid, cfg.reduction)
+    if cfg.softcap_T <= 0:
+        # sum_v d loss / d a_iv = 0 for every valid row, so every column of
+        # grad_W sums to zero.  The bf16 logits and gradients perturb each
+        # row's sum by at most 2^-9 (2 + max|z|) s (first order), hence
+        # |column sum_j| <= m s 2^-9 (2 + max|z|) sum_valid |h_ij|.
+        colsum = o.grad_W.double().sum(0)
+        hv = h.float().index_select(0, torch.from_numpy(np.nonzero(valid)[0]).to(h.device))
+        zmax = float(np.max(np.abs(gold["M"])))
+        bound = cfg.multiplier * s * 2.0 ** -9 * (2.0 + zmax) * hv.abs().double().sum(0)
+        ratio = (colsum.abs() / bound).max().item()
+        log(f"[full] {name}: max |column sum| / bound = {ratio:.3f}")
+        assert ratio <= 1.0
+
+    rng = np.random.default_rng(2024)
+    rows = np.sort(rng.choice(np.nonzero(valid)[0], 64, replace=False))
+    vrows = np.unique(np.concatenate([rng.choice(cfg.V, 64, replace=False),
+                                      rng.choice(case.labels[valid], 64, replace=False)]))
+    W64 = case.W_f32().astype(np.float64)
+    h32 = case.h_f32()
+    gh_ref = oracle.grad_h_rows(h32, W64, case.labels, rows, n_valid, IGN, cfg.softcap_T,
+                                cfg.multiplier, cfg.reduction)
+    gh = o.grad_h.index_select(0, torch.from_numpy(rows).to(h.device)).float().cpu().numpy()
+    e_gh = rel_fro(gh, gh_ref)
+    gW_ref = oracle.grad_W_rows(h32, W64, case.labels, vrows, gold["lse"], n_valid, IGN,
+                                cfg.softcap_T, cfg.multiplier, cfg.reduction)
+    gW = o.grad_W.index_select(0, torch.from_numpy(vrows).to(h.device)).cpu().numpy()
+    e_gW = rel_fro(gW, gW_ref)
+    log(f"[full] {name}: sampled grad_h rel {e_gh:.2e} ({len(rows)} rows), "
+        f"grad_W rel {e_gW:.2e} ({len(vrows)} vocabulary rows)")
+    assert e_gh <= 2e-2
+    assert e_gW <= 2e-2
