@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/flce.h"
+#include "flce.h"
 
 namespace flce {
 

@@ -72,206 +72,257 @@ __device__ __forceinline__ void map_tile(const TileMap& t, int& tm, int& tn, int
 }
 
 // ---------------------------------------------------------------------------
+// Global loads are raw buffer loads: a descriptor (base, byte range) lives in
+// scalar registers and each lane supplies a byte offset.  Offsets at or past
+// the range read as zero, so tails and padding need no branches; an offset of
+// kOOB is always past the range.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int64_t kMaxRange = 0x7FFFFFFF;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // Loader for an operand stored [mn][k] with k contiguous (row stride `ld`
 // bytes).  Thread t moves chunk (t & 7) of rows (t >> 3) + 32 i, i = 0..7.
-// Rows >= mn_valid and K bytes >= k_bytes read as zero.
+// Rows >= mn_valid and K bytes >= k_bytes read as zero.  The descriptor base
+// advances by one K step per fetch, so the per-lane offsets never change.
 struct KMajorLoader {
-  const char* p;
-  int64_t rstride;
-  int64_t kbyte;
+  const char* base;
+  int64_t range0;    // valid bytes from the tile base (all valid rows)
+  int64_t kpos;      // byte offset of the current K step
   int64_t k_bytes;
-  uint32_t row_mask;
+  int kc16;
+  uint32_t voff[8];
   u32x4 buf[8];
 
-  __device__ __forceinline__ void init(const void* base, int64_t ld, int mn0, int mn_valid,
+  __device__ __forceinline__ void init(const void* base_, int64_t ld, int mn0, int mn_valid,
                                        int64_t k_bytes_, int kstep0) {
     const int t = threadIdx.x;
-    const int r = t >> 3, kc = t & 7;
-    kbyte = (int64_t)kstep0 * kKBytes + kc * 16;
-    p = static_cast<const char*>(base) + (int64_t)(mn0 + r) * ld + kbyte;
-    rstride = 32 * ld;
+    const int r = t >> 3;
+    kc16 = (t & 7) * 16;
+    int rows = mn_valid - mn0;
+    rows = rows < 0 ? 0 : (rows > kTile ? kTile : rows);
+    base = static_cast<const char*>(base_) + (int64_t)mn0 * ld;
+    range0 = (int64_t)rows * ld;
+    kpos = (int64_t)kstep0 * kKBytes;
     k_bytes = k_bytes_;
-    row_mask = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) row_mask |= (mn0 + r + 32 * i < mn_valid) ? (1u << i) : 0u;
+    for (int i = 0; i < 8; ++i)
+      voff[i] = (r + 32 * i < rows) ? (uint32_t)((r + 32 * i) * ld + kc16) : kOOB;
   }
+  __amdgpu_buffer_rsrc_t rs;
+  bool kok;
+  // fetch = begin_fetch + fetch_part(0..7) + end_fetch; store = store_part(0..7)
+  __device__ __forceinline__ void begin_fetch() {
+    rs = make_rsrc(base + kpos, range0 - kpos);
+    kok = kpos + kc16 < k_bytes;
+  }
+  __device__ __forceinline__ void fetch_part(int i) { buf[i] = load16(rs, kok ? voff[i] : kOOB); }
+  __device__ __forceinline__ void end_fetch() { kpos += kKBytes; }
   __device__ __forceinline__ void fetch() {
-    const bool kok = kbyte < k_bytes;
+    begin_fetch();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (kok && ((row_mask >> i) & 1u)) v = *reinterpret_cast<const u32x4*>(p + i * rstride);
-      buf[i] = v;
-    }
-    p += kKBytes;
-    kbyte += kKBytes;
+    for (int i = 0; i < 8; ++i) fetch_part(i);
+    end_fetch();
+  }
+  __device__ __forceinline__ void store_part(char* lds, int i) const {
+    const int t = threadIdx.x;
+    *reinterpret_cast<u32x4*>(lds + lds_offset((t >> 3) + 32 * i, t & 7)) = buf[i];
   }
   __device__ __forceinline__ void store(char* lds) const {
-    const int t = threadIdx.x;
-    const int r = t >> 3, kc = t & 7;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(lds + lds_offset(r + 32 * i, kc)) = buf[i];
+    for (int i = 0; i < 8; ++i) store_part(lds, i);
   }
 };
 
 // Loader for an operand stored [k][mn] with mn contiguous: the tile is read
 // in 16-byte row pieces and transposed in registers so that LDS again holds K
 // contiguous per mn row.  mn_valid must be a multiple of the chunk width.
+// The descriptor is rebased at the first K row of each step; rows past
+// k_valid fall outside its range.
 template <typename T> struct MNMajorLoader;
 
 // bf16: thread t moves the 8 x 8 block k = 8 (t >> 5) + 0..7, mn = 8 (t & 31) + 0..7.
 template <> struct MNMajorLoader<bf16> {
-  const char* p;
+  const char* base;
   int64_t ld;
-  int krow, k_valid;
-  bool mn_ok;
+  int krow0, k_valid;
+  uint32_t voff[8];
   u32x4 buf[8];
 
-  __device__ __forceinline__ void init(const void* base, int64_t ld_, int mn0, int mn_valid,
+  __device__ __forceinline__ void init(const void* base_, int64_t ld_, int mn0, int mn_valid,
                                        int k_valid_, int kstep0) {
     const int t = threadIdx.x;
     const int kb = t >> 5, mb = t & 31;
     ld = ld_;
-    krow = kstep0 * 64 + kb * 8;
+    base = static_cast<const char*>(base_);
+    krow0 = kstep0 * 64;
     k_valid = k_valid_;
-    mn_ok = mn0 + mb * 8 < mn_valid;
-    p = static_cast<const char*>(base) + (int64_t)krow * ld + (int64_t)(mn0 + mb * 8) * 2;
-  }
-  __device__ __forceinline__ void fetch() {
+    const bool mn_ok = mn0 + mb * 8 < mn_valid;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (mn_ok && krow + j < k_valid) v = *reinterpret_cast<const u32x4*>(p + j * ld);
-      buf[j] = v;
-    }
-    p += 64 * ld;
-    krow += 64;
+    for (int j = 0; j < 8; ++j)
+      voff[j] = mn_ok ? (uint32_t)((kb * 8 + j) * ld + (int64_t)(mn0 + mb * 8) * 2) : kOOB;
   }
-  __device__ __forceinline__ void store(char* lds) const {
+  __amdgpu_buffer_rsrc_t rs;
+  __device__ __forceinline__ void begin_fetch() {
+    rs = make_rsrc(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
+  }
+  __device__ __forceinline__ void fetch_part(int j) { buf[j] = load16(rs, voff[j]); }
+  __device__ __forceinline__ void end_fetch() { krow0 += 64; }
+  __device__ __forceinline__ void fetch() {
+    begin_fetch();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fetch_part(j);
+    end_fetch();
+  }
+  // buf[j] holds mn = 0..7 of k row j (dword d: mn 2d low half, 2d+1 high half).
+  // Output chunk c holds k = 0..7 of mn column c (dword e: k 2e low, 2e+1 high).
+  __device__ __forceinline__ void store_part(char* lds, int c) const {
     const int t = threadIdx.x;
     const int kb = t >> 5, mb = t & 31;
-    // buf[j] holds mn = 0..7 of k row j (dword d: mn 2d low half, 2d+1 high half).
-    // Output chunk c holds k = 0..7 of mn column c (dword e: k 2e low, 2e+1 high).
+    u32x4 o;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      u32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = buf[2 * e][c >> 1], y = buf[2 * e + 1][c >> 1];
-        o[e] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-      }
-      *reinterpret_cast<u32x4*>(lds + lds_offset(mb * 8 + c, kb)) = o;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x = buf[2 * e][c >> 1], y = buf[2 * e + 1][c >> 1];
+      o[e] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
     }
+    *reinterpret_cast<u32x4*>(lds + lds_offset(mb * 8 + c, kb)) = o;
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) store_part(lds, c);
   }
 };
 
 // fp32: thread t moves two 4 x 4 blocks b = t + 256 u: k = 4 (b >> 6) + 0..3,
 // mn = 4 (b & 63) + 0..3.
 template <> struct MNMajorLoader<float> {
-  const char* p[2];
+  const char* base;
   int64_t ld;
-  int krow[2], k_valid;
-  bool mn_ok;
+  int krow0, k_valid;
+  uint32_t voff[8];
   u32x4 buf[8];
 
-  __device__ __forceinline__ void init(const void* base, int64_t ld_, int mn0, int mn_valid,
+  __device__ __forceinline__ void init(const void* base_, int64_t ld_, int mn0, int mn_valid,
                                        int k_valid_, int kstep0) {
     const int t = threadIdx.x;
     const int mb = t & 63;
     ld = ld_;
+    base = static_cast<const char*>(base_);
+    krow0 = kstep0 * 32;
     k_valid = k_valid_;
-    mn_ok = mn0 + mb * 4 < mn_valid;
+    const bool mn_ok = mn0 + mb * 4 < mn_valid;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kb = (t >> 6) + 4 * u;
-      krow[u] = kstep0 * 32 + kb * 4;
-      p[u] = static_cast<const char*>(base) + (int64_t)krow[u] * ld + (int64_t)(mn0 + mb * 4) * 4;
-    }
-  }
-  __device__ __forceinline__ void fetch() {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (mn_ok && krow[u] + j < k_valid) v = *reinterpret_cast<const u32x4*>(p[u] + j * ld);
-        buf[4 * u + j] = v;
+        const int kr = ((t >> 6) + 4 * u) * 4 + j;
+        voff[4 * u + j] = mn_ok ? (uint32_t)(kr * ld + (int64_t)(mn0 + mb * 4) * 4) : kOOB;
       }
-      p[u] += 32 * ld;
-      krow[u] += 32;
-    }
+  }
+  __amdgpu_buffer_rsrc_t rs;
+  __device__ __forceinline__ void begin_fetch() {
+    rs = make_rsrc(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
+  }
+  __device__ __forceinline__ void fetch_part(int j) { buf[j] = load16(rs, voff[j]); }
+  __device__ __forceinline__ void end_fetch() { krow0 += 32; }
+  __device__ __forceinline__ void fetch() {
+    begin_fetch();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fetch_part(j);
+    end_fetch();
+  }
+  // part p: block u = p >> 2, column c = p & 3
+  __device__ __forceinline__ void store_part(char* lds, int p) const {
+    const int t = threadIdx.x;
+    const int u = p >> 2, c = p & 3;
+    const int kb = (t >> 6) + 4 * u;
+    u32x4 o = {buf[4 * u + 0][c], buf[4 * u + 1][c], buf[4 * u + 2][c], buf[4 * u + 3][c]};
+    *reinterpret_cast<u32x4*>(lds + lds_offset((t & 63) * 4 + c, kb)) = o;
   }
   __device__ __forceinline__ void store(char* lds) const {
-    const int t = threadIdx.x;
-    const int mb = t & 63;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kb = (t >> 6) + 4 * u;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 o = {buf[4 * u + 0][c], buf[4 * u + 1][c], buf[4 * u + 2][c], buf[4 * u + 3][c]};
-        *reinterpret_cast<u32x4*>(lds + lds_offset(mb * 4 + c, kb)) = o;
-      }
-    }
+    for (int p = 0; p < 8; ++p) store_part(lds, p);
   }
 };
 
 // ---------------------------------------------------------------------------
-// One chunk of K for every block of the wave's quadrant.  Operands are
-// reinterpreted as whole vectors (a bit cast of a single vector element is not
-// used: it does not select the element).  The fp32 form issues the chunk's 4
-// K slots outermost so that consecutive MFMAs write different accumulators.
-__device__ __forceinline__ void mma_quadrant(f32x16 (&acc)[4][4], const u32x4 (&a)[4],
-                                             const u32x4 (&b)[4], bf16) {
+// MFMAs of one block row (bm) of the wave's quadrant for one chunk of K.
+// Operands are reinterpreted as whole vectors (a bit cast of a single vector
+// element is not used: it does not select the element).
+__device__ __forceinline__ void mma_row(f32x16 (&acc)[4][4], const u32x4& a, const u32x4 (&b)[4], int bm,
+                                        bf16) {
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
-      acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[bm]),
-                                                            __builtin_bit_cast(bf16x8, b[bn]),
-                                                            acc[bm][bn], 0, 0, 0);
+  for (int bn = 0; bn < 4; ++bn)
+    acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, b[bn]),
+                                                          acc[bm][bn], 0, 0, 0);
 }
-__device__ __forceinline__ void mma_quadrant(f32x16 (&acc)[4][4], const u32x4 (&a)[4],
-                                             const u32x4 (&b)[4], float) {
-  f32x4 af[4], bf[4];
+// fp32: the chunk's 4 K values feed 4 MFMAs of K = 2, issued slot-outermost so
+// that consecutive MFMAs write different accumulators.
+__device__ __forceinline__ void mma_row(f32x16 (&acc)[4][4], const u32x4& a, const u32x4 (&b)[4], int bm,
+                                        float) {
+  const f32x4 af = __builtin_bit_cast(f32x4, a);
+  f32x4 bf[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    af[i] = __builtin_bit_cast(f32x4, a[i]);
-    bf[i] = __builtin_bit_cast(f32x4, b[i]);
-  }
+  for (int bn = 0; bn < 4; ++bn) bf[bn] = __builtin_bit_cast(f32x4, b[bn]);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-        acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[bm][e], bf[bn][e], acc[bm][bn], 0, 0, 0);
-}
-
-// One K step (four sub-steps of two chunks) of the wave's 128 x 128 quadrant.
-template <typename T>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[4][4], const char* As, const char* Bs,
-                                          int wm, int wn, int lane) {
-  const int lo = lane & 31, hi = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 a[4], b[4];
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-      a[bm] = *reinterpret_cast<const u32x4*>(As + lds_offset(wm * 128 + bm * 32 + lo, 2 * ks + hi));
-#pragma unroll
     for (int bn = 0; bn < 4; ++bn)
-      b[bn] = *reinterpret_cast<const u32x4*>(Bs + lds_offset(wn * 128 + bn * 32 + lo, 2 * ks + hi));
-    mma_quadrant(acc, a, b, T{});
-  }
+      acc[bm][bn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[bn][e], acc[bm][bn], 0, 0, 0);
 }
 
-// Full K loop: acc = sum over nk K steps of A_tile * B_tile^T.  Ends with a
-// barrier, after which the LDS may be reused by the epilogue.
+// Per-lane LDS byte offsets of the wave's fragments: A rows wm*128 + bm*32 +
+// (l & 31), B rows wn*128 + bn*32 + (l & 31), chunk 2 ks + (l >> 5).
+struct FragAddr {
+  int a[4][4];   // [bm][ks]
+  int b[4][4];   // [bn][ks]
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    const int lo = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        a[i][ks] = lds_offset(wm * 128 + i * 32 + lo, 2 * ks + hi);
+        b[i][ks] = kOperandStage + lds_offset(wn * 128 + i * 32 + lo, 2 * ks + hi);
+      }
+  }
+};
+
+__device__ __forceinline__ u32x4 lds_read16(const char* stage, int off) {
+  return *reinterpret_cast<const u32x4*>(stage + off);
+}
+
+#define FLCE_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Full K loop: acc = sum over nk K steps of A_tile * B_tile^T.
+//
+// A K step is four sub-steps of 16 MFMAs (4 block rows x 4 block columns),
+// each split into four groups of one block row; fences keep the program
+// order.  Alongside the MFMAs of sub-step s, the fragments of sub-step s + 1
+// are read (B fragments first, so that every MFMA's operands were requested
+// at least 8 MFMAs earlier):
+//   sub-step 0: -
+//   sub-step 1: write the registers fetched one step earlier to the other
+//               LDS stage (4 chunks per group)
+//   sub-step 2: issue the loads for two steps ahead (4 per group)
+//   barrier: everyone is done reading this stage and writing the other
+//   sub-step 3: its fragments come from registers; read sub-step 0 of the
+//               next stage.
+// Fetches and stores run every step (past the last K step the loads are out
+// of range and read zeros).  Ends with a barrier, after which the LDS may be
+// reused by the epilogue.
 template <typename T, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  FragAddr fa;
+  fa.init(wave >> 1, wave & 1, lane);
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
@@ -283,22 +334,65 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
   lb.fetch();
   la.store(smem);
   lb.store(smem + kOperandStage);
+  la.fetch();
+  lb.fetch();
   __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    char* cur = smem + (it & 1) * kStageBytes;
-    char* nxt = smem + ((it & 1) ^ 1) * kStageBytes;
-    const bool more = it + 1 < nk;
-    if (more) {
-      la.fetch();
-      lb.fetch();
-    }
-    mma_stage<T>(acc, cur, cur + kOperandStage, wm, wn, lane);
-    if (more) {
-      la.store(nxt);
-      lb.store(nxt + kOperandStage);
-    }
-    __syncthreads();
+  u32x4 a[2][4], b[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[0][i] = lds_read16(smem, fa.b[i][0]);
+    a[0][i] = lds_read16(smem, fa.a[i][0]);
   }
+  for (int it = 0; it < nk; ++it) {
+    const char* cur = smem + (it & 1) * kStageBytes;
+    char* nxt = smem + ((it & 1) ^ 1) * kStageBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int p = ks & 1, q = p ^ 1;
+      if (ks == 2) {
+        la.begin_fetch();
+        lb.begin_fetch();
+      }
+      if (ks == 3) {
+        FLCE_FENCE();
+        __syncthreads();
+        FLCE_FENCE();
+      }
+      const char* src = ks == 3 ? nxt : cur;
+      const int nks = (ks + 1) & 3;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        FLCE_FENCE();
+        mma_row(acc, a[p][g], b[p], g, T{});
+        // fragments of the next sub-step: B first (groups 0-1), then A (2-3)
+        if (g < 2) {
+          b[q][2 * g] = lds_read16(src, fa.b[2 * g][nks]);
+          b[q][2 * g + 1] = lds_read16(src, fa.b[2 * g + 1][nks]);
+        } else {
+          a[q][2 * g - 4] = lds_read16(src, fa.a[2 * g - 4][nks]);
+          a[q][2 * g - 3] = lds_read16(src, fa.a[2 * g - 3][nks]);
+        }
+        if (ks == 1) {
+          la.store_part(nxt, 2 * g);
+          la.store_part(nxt, 2 * g + 1);
+          lb.store_part(nxt + kOperandStage, 2 * g);
+          lb.store_part(nxt + kOperandStage, 2 * g + 1);
+        }
+        if (ks == 2) {
+          la.fetch_part(2 * g);
+          la.fetch_part(2 * g + 1);
+          lb.fetch_part(2 * g);
+          lb.fetch_part(2 * g + 1);
+        }
+      }
+      if (ks == 2) {
+        la.end_fetch();
+        lb.end_fetch();
+      }
+    }
+  }
+  FLCE_FENCE();
+  __syncthreads();
 }
 
 }  // namespace flce
