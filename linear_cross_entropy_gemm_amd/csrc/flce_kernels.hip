@@ -239,39 +239,74 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// grad_W (+)= G^T h_c: rows = vocabulary (M), cols = hidden (N), K = tokens.
-// Both operands are stored with K as the slow dimension and are transposed
-// through registers.
+// grad_W (+)= G^T h_c, computed as its transpose h_c^T G: rows = hidden (M),
+// cols = vocabulary (N), K = tokens.  Both operands are stored with K as the
+// slow dimension and are transposed through registers.  With hidden on the M
+// side each lane owns 4 consecutive hidden entries of one vocabulary row of
+// grad_W per accumulator group, so the fp32 epilogue moves 16 bytes per
+// access; the read-modify-write of later chunks keeps the loads of the next
+// block row in flight while the current one is added and stored.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
   MNMajorLoader<T> la, lb;
-  la.init(p.G, p.ldg, tm * kTile, p.Vp, p.C_this, 0);
-  lb.init(p.h, p.ldh, tn * kTile, p.H, p.C_this, 0);
+  la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);
+  lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0);
   constexpr int bk = kKBytes / Elem<T>::size;
   const int nk = (p.C_this + bk - 1) / bk;
   f32x16 acc[4][4];
   gemm_mainloop<T>(la, lb, nk, smem, acc);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
+  // element (bm, bn, i): vocabulary row n, hidden entries m .. m + 3
+  const int n0 = tn * kTile + wn * 128 + lo;
+  const int m0 = tm * kTile + wm * 128 + 4 * hi;
+  auto ptr = [&](int bm, int bn, int i) -> f32x4* {
+    return reinterpret_cast<f32x4*>(p.gW + (int64_t)(n0 + bn * 32) * p.H + m0 + bm * 32 + 8 * i);
+  };
+  // vector (bm, bn, i) covers hidden m .. m + 3 with m a multiple of 4 and
+  // H a multiple of 4, so m < H keeps the whole vector inside the row
+  auto vec_ok = [&](int bm, int bn, int i) { return n0 + bn * 32 < p.V && m0 + bm * 32 + 8 * i < p.H; };
+  if (!p.accumulate) {
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int col = tn * kTile + wn * 128 + bn * 32 + lo;
+      for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = tm * kTile + wm * 128 + bm * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-        if (row < p.V && col < p.H) {
-          float* dst = p.gW + (int64_t)row * p.H + col;
-          float val = acc[bm][bn][v];
-          if (p.accumulate) val += *dst;
-          *dst = val;
-        }
-      }
+        for (int i = 0; i < 4; ++i)
+          if (vec_ok(bm, bn, i))
+            *ptr(bm, bn, i) = f32x4{acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1], acc[bm][bn][4 * i + 2],
+                                    acc[bm][bn][4 * i + 3]};
+    return;
+  }
+  f32x4 old[2][16];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      old[0][bn * 4 + i] = vec_ok(0, bn, i) ? *ptr(0, bn, i) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+    const int cb = bm & 1;
+    if (bm + 1 < 4) {
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          old[cb ^ 1][bn * 4 + i] = vec_ok(bm + 1, bn, i) ? *ptr(bm + 1, bn, i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (vec_ok(bm, bn, i)) {
+          const f32x4 o = old[cb][bn * 4 + i];
+          *ptr(bm, bn, i) = f32x4{o[0] + acc[bm][bn][4 * i], o[1] + acc[bm][bn][4 * i + 1],
+                                  o[2] + acc[bm][bn][4 * i + 2], o[3] + acc[bm][bn][4 * i + 3]};
+        }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -403,7 +438,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     f.z = zbuf; f.ldz = (int64_t)Vp * es;
     f.pmax = pmax; f.psum = psum; f.parg = parg; f.ldp = C;
     f.zlab = zlab + c0;
-    f.map = TileMap{tiles_voc, tiles_tok, 1, 1, 0};
+    f.map = TileMap{tiles_voc, tiles_tok, 1, 1, 0, 0};
     {
       ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
       fwd_logits_kernel<T><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(f);
@@ -435,7 +470,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gh.ksteps_per_split = (gh.ksteps_total + (int)pl.split_k - 1) / (int)pl.split_k;
     const int splits = (gh.ksteps_total + gh.ksteps_per_split - 1) / gh.ksteps_per_split;
     gh.part = ghpart; gh.part_stride = (int64_t)C * H;
-    gh.map = TileMap{tiles_tok, tiles_hid, splits, tiles_tok, 0};
+    gh.map = TileMap{tiles_tok, tiles_hid, splits, tiles_tok, 0, 0};
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_H, st);
       grad_h_kernel<T><<<tiles_tok * tiles_hid * splits, kThreads, 0, st>>>(gh);
@@ -454,10 +489,10 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gw.G = zbuf; gw.ldg = (int64_t)Vp * es; gw.h = hc; gw.ldh = a.H * es;
     gw.C_this = Ct; gw.H = H; gw.V = V; gw.Vp = Vp;
     gw.gW = a.grad_W; gw.accumulate = ck > 0 ? 1 : 0;
-    gw.map = TileMap{tiles_voc, tiles_hid, 1, 4, 1};
+    gw.map = TileMap{tiles_hid, tiles_voc, 1, 4, 1, 1};
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_W, st);
-      grad_W_kernel<T><<<tiles_voc * tiles_hid, kThreads, 0, st>>>(gw);
+      grad_W_kernel<T><<<tiles_hid * tiles_voc, kThreads, 0, st>>>(gw);
     }
   }
   FinalizeArgs fa;

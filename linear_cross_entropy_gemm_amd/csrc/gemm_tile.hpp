@@ -47,8 +47,10 @@ __device__ __forceinline__ int lds_offset(int row, int chunk) {
 //   group_m: within a split, tiles are walked in groups of group_m M-tiles
 //     by all N-tiles, M fastest inside a group (group_m = 1: N fastest;
 //     group_m >= tiles_m: M fastest over the whole column).
+//   swap_walk: walk as if M and N were exchanged (groups of N-tiles by all
+//     M-tiles), for kernels whose reused operand sits on the N side.
 struct TileMap {
-  int tiles_m, tiles_n, splits, group_m, xcd_contiguous;
+  int tiles_m, tiles_n, splits, group_m, xcd_contiguous, swap_walk;
 };
 
 __device__ __forceinline__ void map_tile(const TileMap& t, int& tm, int& tn, int& split) {
@@ -62,13 +64,17 @@ __device__ __forceinline__ void map_tile(const TileMap& t, int& tm, int& tn, int
   const int per_split = t.tiles_m * t.tiles_n;
   split = L / per_split;
   L -= split * per_split;
-  const int gsz = t.group_m * t.tiles_n;
+  const int wm = t.swap_walk ? t.tiles_n : t.tiles_m;
+  const int wn = t.swap_walk ? t.tiles_m : t.tiles_n;
+  const int gsz = t.group_m * wn;
   const int g = L / gsz;
   const int r = L - g * gsz;
-  const int rows_left = t.tiles_m - g * t.group_m;
+  const int rows_left = wm - g * t.group_m;
   const int gm = rows_left < t.group_m ? rows_left : t.group_m;
-  tm = g * t.group_m + r % gm;
-  tn = r / gm;
+  const int a = g * t.group_m + r % gm;
+  const int b = r / gm;
+  tm = t.swap_walk ? b : a;
+  tn = t.swap_walk ? a : b;
 }
 
 // ---------------------------------------------------------------------------

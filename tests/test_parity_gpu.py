@@ -181,3 +181,42 @@ def test_autograd_wrapper_scales_by_upstream_gradient():
     assert abs(loss.item() - ref["loss"]) / ref["loss"] <= 1e-5
     assert rel_fro(h.grad.cpu().numpy(), 3.0 * ref["grad_h"]) <= 1e-4
     assert rel_fro(W.grad.cpu().numpy(), 3.0 * ref["grad_W"]) <= 1e-4
+
+
+@pytest.mark.parametrize("base,N,H,V", [("c2", 300, 8, 300), ("c2", 257, 24, 1000), ("c1", 130, 4, 260),
+                                        ("c1", 77, 36, 513), ("c4", 600, 264, 777)])
+def test_outputs_stay_inside_their_buffers(base, N, H, V):
+    """Every output sits inside a larger allocation filled with a canary
+    pattern; after the call the canaries on both sides are unchanged."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make(base, N, H, V, 1.0, 0.5, "mean")
+    log(f"[canary] {case.cfg.dtype} N={N} H={H} V={V}")
+    h, W, lab = to_device(case)
+    dev = h.device
+    PAD = 4096  # bytes of canary on each side (multiple of 256 keeps alignment)
+
+    def guarded(nbytes):
+        buf = torch.full((nbytes + 2 * PAD,), 0xA5, dtype=torch.uint8, device=dev)
+        return buf, buf[PAD:PAD + nbytes]
+
+    es = 2 if case.cfg.dtype == "bf16" else 4
+    dt = L.FLCE_DTYPE_BF16 if es == 2 else L.FLCE_DTYPE_F32
+    ws_bytes = L.flce_workspace_size(N, H, V, dt, 0)
+    bufs = {k: guarded(n) for k, n in [("loss", 4), ("nc", 8), ("gh", N * H * es), ("gW", V * H * 4),
+                                       ("ws", ws_bytes)]}
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = L.flce_fwd_bwd(h.data_ptr(), W.data_ptr(), lab.data_ptr(), N, H, V, synth.IGNORE_INDEX, 1.0, 0.5,
+                        L.FLCE_REDUCTION_MEAN, bufs["loss"][1].data_ptr(), bufs["gh"][1].data_ptr(),
+                        bufs["gW"][1].data_ptr(), bufs["nc"][1].data_ptr(), stream, dt,
+                        bufs["ws"][1].data_ptr(), ws_bytes)
+    torch.cuda.synchronize()
+    assert rc == L.FLCE_OK
+    for k, (buf, inner) in bufs.items():
+        n = inner.numel()
+        head = buf[:PAD]
+        tail = buf[PAD + n:]
+        assert bool((head == 0xA5).all()) and bool((tail == 0xA5).all()), f"write outside {k}"
+    ref = reference(case)
+    gW = bufs["gW"][1].view(torch.float32).view(V, H).cpu().numpy()
+    assert rel_fro(gW, ref["grad_W"]) <= tolerances(case.cfg.dtype)[1]
