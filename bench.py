@@ -78,7 +78,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--cpu-tokens", type=int, default=192)
+    ap.add_argument("--cpu-tokens", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
