@@ -116,12 +116,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
   const int64_t kbytes = (int64_t)p.H * Elem<T>::size;
-  KMajorLoader la, lb;
-  la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0);
-  lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0);
   f32x16 acc[4][4];
-  const int nk = (int)((kbytes + kKBytes - 1) / kKBytes);
-  gemm_mainloop<T>(la, lb, nk, smem, acc);
+  if constexpr (sizeof(T) == 2) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    KMajorDirect la, lb;
+    la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0, (wave >> 1) * 128, lane);
+    lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, (int)((kbytes + kDKBytes - 1) / kDKBytes), smem, acc);
+  } else {
+    KMajorLoader la, lb;
+    la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0);
+    lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0);
+    gemm_mainloop<T>(la, lb, (int)((kbytes + kKBytes - 1) / kKBytes), smem, acc);
+  }
   fwd_epilogue<T>(acc, p, tm, tn, smem);
 }
 
@@ -207,12 +214,22 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
   const int k0 = sp * p.ksteps_per_split;
   const int rem = p.ksteps_total - k0;
   const int nk = rem < p.ksteps_per_split ? rem : p.ksteps_per_split;
-  KMajorLoader la;
-  la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * Elem<T>::size, k0);
-  MNMajorLoader<T> lb;
-  lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0);
   f32x16 acc[4][4];
-  gemm_mainloop<T>(la, lb, nk, smem, acc);
+  if constexpr (sizeof(T) == 2) {
+    // the split is planned in 128-byte K steps; the direct pipeline runs 64-byte steps
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    KMajorDirect la;
+    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, 2 * k0, (wave >> 1) * 128, lane);
+    MNMajorDirect lb;
+    lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, 2 * k0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, 2 * nk, smem, acc);
+  } else {
+    KMajorLoader la;
+    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * Elem<T>::size, k0);
+    MNMajorLoader<T> lb;
+    lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0);
+    gemm_mainloop<T>(la, lb, nk, smem, acc);
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
   float* out = p.part + (int64_t)sp * p.part_stride;
@@ -251,13 +268,20 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
-  MNMajorLoader<T> la, lb;
-  la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);
-  lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0);
-  constexpr int bk = kKBytes / Elem<T>::size;
-  const int nk = (p.C_this + bk - 1) / bk;
   f32x16 acc[4][4];
-  gemm_mainloop<T>(la, lb, nk, smem, acc);
+  if constexpr (sizeof(T) == 2) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    MNMajorDirect la, lb;
+    la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0, (wave >> 1) * 128, lane);
+    lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, (p.C_this + 31) / 32, smem, acc);
+  } else {
+    MNMajorLoader<T> la, lb;
+    la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);
+    lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0);
+    constexpr int bk = kKBytes / Elem<T>::size;
+    gemm_mainloop<T>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
   // element (bm, bn, i): vocabulary row n, hidden entries m .. m + 3

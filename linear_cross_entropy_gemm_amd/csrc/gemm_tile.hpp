@@ -401,4 +401,232 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
   __syncthreads();
 }
 
+// ===========================================================================
+// bf16 pipeline with direct-to-LDS loads.
+//
+// Global tiles go straight into LDS with buffer_load_dwordx4 ... lds (lane l
+// of an instruction fills the 16 bytes at M0 + 16 l; out-of-range offsets
+// fill zeros), so no registers stage the operands and no LDS store
+// instructions are issued.  The LDS holds a ring of 4 stages of 32 K
+// (64 bytes of K per operand row, 32 KiB per stage for A + B), loaded three K
+// steps ahead.
+//
+// K-major operand stage (rows = M or N index, 4 chunks of 16 bytes of K per
+// row): rows 2L and 2L+1 share the 128-byte line L; chunk c of row r sits in
+// slot ((r & 1) * 4 + c) ^ (L & 7) of its line, so 8 consecutive rows reading
+// the same chunk hit 8 different bank groups.
+//
+// MN-major operand stage (rows = K index, 256 MN values = 512 bytes per row):
+// 16-byte unit u of row k sits at unit u ^ (2 (k & 3)).  A fragment is read
+// with two ds_read_b64_tr_b16: in each 16-lane group, lane p fetches 4
+// consecutive MN values of K row k0 + (p >> 2); the hardware hands lane p the
+// 4 K values of MN column (p) -- the same lane -> (row, K) assignment as a
+// K-major 16-byte fragment read.
+constexpr int kDStages = 4;
+constexpr int kDKBytes = 64;
+constexpr int kDOperand = kTile * kDKBytes;   // 16 KiB
+constexpr int kDStage = 2 * kDOperand;        // 32 KiB
+static_assert(kDStages * kDStage == kLdsBytes, "LDS ring size");
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define FLCE_AS3 __attribute__((address_space(3)))
+
+// Buffer descriptor as four scalar dwords (base, stride 0, byte range, raw
+// dword format) for the direct-to-LDS load below.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4s make_rsrc_words(const char* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)n, 0x00020000u};
+}
+
+// One direct-to-LDS load: lane l's 16 bytes at byte offset voff of the buffer
+// land at LDS address lds + 16 l (zeros when voff is out of range).  Written
+// as inline assembly so that the compiler does not treat it as an LDS write
+// that every later LDS read must wait for: the K loop orders these loads
+// itself with explicit vmcnt waits and barriers, and waits for all of them
+// (vmcnt(0)) before the LDS is reused.
+__device__ __forceinline__ void lds_dma16(const u32x4s& r, char* lds, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((FLCE_AS3 char*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ int kd_offset(int r, int c) {
+  const int L = r >> 1;
+  return L * 128 + (((((r & 1) << 2) | c) ^ (L & 7)) << 4);
+}
+
+// K-major operand [mn][k] (k contiguous, row stride `ld` bytes).
+struct KMajorDirect {
+  const char* base;
+  int64_t range0, kpos, k_bytes;
+  uint32_t voff[4];
+  int c16[4];
+  int frag[2];   // per-lane fragment offsets for sub-steps 0 and 1 (block 0)
+
+  __device__ __forceinline__ void init(const void* base_, int64_t ld, int mn0, int mn_valid, int64_t k_bytes_,
+                                       int kstep0, int row0, int lane) {
+    const int t = threadIdx.x, w = t >> 6, lam = t & 63;
+    int rows = mn_valid - mn0;
+    rows = rows < 0 ? 0 : (rows > kTile ? kTile : rows);
+    base = static_cast<const char*>(base_) + (int64_t)mn0 * ld;
+    range0 = (int64_t)rows * ld;
+    kpos = (int64_t)kstep0 * kDKBytes;
+    k_bytes = k_bytes_;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int L = (4 * w + j) * 8 + (lam >> 3);
+      const int x = (lam & 7) ^ (L & 7);
+      const int r = 2 * L + (x >> 2), c = x & 3;
+      voff[j] = r < rows ? (uint32_t)(r * ld + c * 16) : kOOB;
+      c16[j] = c * 16;
+    }
+    const int lo = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) frag[ks] = kd_offset(row0 + lo, 2 * ks + hi);
+  }
+  // Issue this wave's 4 loads of the next K step into `stage` (16 KiB).
+  __device__ __forceinline__ void issue_part(char* stage, int j) {
+    const u32x4s rs = make_rsrc_words(base + kpos, range0 - kpos);
+    const uint32_t off = kpos + c16[j] < k_bytes ? voff[j] : kOOB;
+    lds_dma16(rs, stage + ((threadIdx.x >> 6) * 4 + j) * 1024, off);
+  }
+  __device__ __forceinline__ void advance() { kpos += kDKBytes; }
+  // Fragment of block b (rows row0 + 32 b + (l & 31)) for sub-step ks.
+  __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
+    return *reinterpret_cast<const u32x4*>(stage + frag[ks] + b * 2048);
+  }
+};
+
+// MN-major operand [k][mn] (mn contiguous, row stride `ld` bytes).
+struct MNMajorDirect {
+  const char* base;
+  int64_t ld;
+  int krow0, k_valid;
+  uint32_t voff[4];
+  int frag[2];   // per-lane offsets for even and odd blocks (sub-step 0, first half)
+
+  __device__ __forceinline__ void init(const void* base_, int64_t ld_, int mn0, int mn_valid, int k_valid_,
+                                       int kstep0, int row0, int lane) {
+    const int t = threadIdx.x, w = t >> 6, lam = t & 63;
+    ld = ld_;
+    base = static_cast<const char*>(base_);
+    krow0 = kstep0 * 32;
+    k_valid = k_valid_;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kr = 8 * w + 2 * j + (lam >> 5);
+      const int u = (lam & 31) ^ ((kr & 3) << 1);
+      voff[j] = mn0 + 8 * u < mn_valid ? (uint32_t)(kr * ld + (int64_t)(mn0 + 8 * u) * 2) : kOOB;
+    }
+    const int g = lane >> 4, p = lane & 15;
+    const int f = (p >> 2) << 1;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int x = 2 * (g & 1) + ((p & 3) >> 1);
+      frag[par] = (8 * (g >> 1) + (p >> 2)) * 512 + ((((4 * par + x) ^ f)) << 4) + (p & 1) * 8 + row0 * 2;
+    }
+  }
+  __device__ __forceinline__ void issue_part(char* stage, int j) {
+    const u32x4s rs = make_rsrc_words(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
+    lds_dma16(rs, stage + ((threadIdx.x >> 6) * 4 + j) * 1024, voff[j]);
+  }
+  __device__ __forceinline__ void advance() { krow0 += 32; }
+  __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
+    const char* q = stage + frag[b & 1] + ks * 8192 + (b >> 1) * 128;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLCE_AS3 i16x4*)(q));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLCE_AS3 i16x4*)(q + 4 * 512));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  }
+};
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+#define FLCE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
+// ... and also every LDS access of this wave (lgkmcnt = 0): before a barrier
+// after which other waves refill the stage this wave has just read.
+#define FLCE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
+
+// K loop of the direct-to-LDS pipeline.  Per K step (2 sub-steps of 16 MFMAs
+// per wave): sub-step 0 runs while the fragments of sub-step 1 are read and
+// the 8 loads three steps ahead are issued; then the wave waits for the next
+// stage's loads, and the barrier both publishes that stage and frees the one
+// just read; sub-step 1 runs while sub-step 0 of the next stage is read.
+template <class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bm][bn][v] = 0.0f;
+  if (nk <= 0) return;
+#pragma unroll
+  for (int s = 0; s < kDStages - 1; ++s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) la.issue_part(smem + s * kDStage, j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lb.issue_part(smem + s * kDStage + kDOperand, j);
+    la.advance();
+    lb.advance();
+  }
+  FLCE_WAIT_VMCNT(16);
+  __syncthreads();
+  u32x4 a[2][4], b[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[0][i] = lb.read(smem + kDOperand, i, 0);
+    a[0][i] = la.read(smem, i, 0);
+  }
+  for (int it = 0; it < nk; ++it) {
+    const char* cur = smem + (it & 3) * kDStage;
+    const char* nxt = smem + ((it + 1) & 3) * kDStage;
+    char* dst = smem + ((it + 3) & 3) * kDStage;
+    // sub-step 0 (+ reads of sub-step 1, + loads for step it + 3)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      FLCE_FENCE();
+      mma_row(acc, a[0][g], b[0], g, bf16{});
+      if (g < 2) {
+        b[1][2 * g] = lb.read(cur + kDOperand, 2 * g, 1);
+        b[1][2 * g + 1] = lb.read(cur + kDOperand, 2 * g + 1, 1);
+        la.issue_part(dst, 2 * g);
+        la.issue_part(dst, 2 * g + 1);
+      } else {
+        a[1][2 * g - 4] = la.read(cur, 2 * g - 4, 1);
+        a[1][2 * g - 3] = la.read(cur, 2 * g - 3, 1);
+        lb.issue_part(dst + kDOperand, 2 * g - 4);
+        lb.issue_part(dst + kDOperand, 2 * g - 3);
+      }
+    }
+    la.advance();
+    lb.advance();
+    FLCE_FENCE();
+    FLCE_WAIT_VMCNT_LDS(16);
+    __syncthreads();
+    FLCE_FENCE();
+    // sub-step 1 (+ reads of sub-step 0 of the next stage)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      FLCE_FENCE();
+      mma_row(acc, a[1][g], b[1], g, bf16{});
+      if (g < 2) {
+        b[0][2 * g] = lb.read(nxt + kDOperand, 2 * g, 0);
+        b[0][2 * g + 1] = lb.read(nxt + kDOperand, 2 * g + 1, 0);
+      } else {
+        a[0][2 * g - 4] = la.read(nxt, 2 * g - 4, 0);
+        a[0][2 * g - 3] = la.read(nxt, 2 * g - 3, 0);
+      }
+    }
+  }
+  FLCE_FENCE();
+  FLCE_WAIT_VMCNT(0);
+  __syncthreads();
+}
+
 }  // namespace flce
