@@ -33,14 +33,16 @@ __device__ __forceinline__ float fast_exp(float x) {
 //  * otherwise tanh|x| = 1 - 2 / (e^{2|x|} + 1), which saturates to 1 as
 //    e^{2|x|} overflows, with the sign restored.
 // Relative error is below 1e-6 over the whole range (tested against fp64).
-__host__ __device__ __forceinline__ float softcap_tanh(float x) {
+__host__ __device__ __forceinline__ float tanh_series(float x) {
   const float x2 = x * x;
   float p = 62.0f / 2835.0f;
   p = p * x2 - 17.0f / 315.0f;
   p = p * x2 + 2.0f / 15.0f;
   p = p * x2 - 1.0f / 3.0f;
   p = p * x2;
-  const float series = x + x * p;
+  return x + x * p;
+}
+__host__ __device__ __forceinline__ float tanh_exp_form(float x) {
   const float ax = __builtin_fabsf(x);
 #if defined(__HIP_DEVICE_COMPILE__)
   const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * ax);
@@ -49,17 +51,21 @@ __host__ __device__ __forceinline__ float softcap_tanh(float x) {
   const float e = __builtin_exp2f(2.0f * kLog2e * ax);
   const float r = 1.0f - 2.0f / (e + 1.0f);
 #endif
-  const float big = __builtin_copysignf(r, x);
-  return ax < 0.25f ? series : big;
+  return __builtin_copysignf(r, x);
+}
+constexpr float kTanhSeriesMax = 0.25f;
+__host__ __device__ __forceinline__ float softcap_tanh(float x) {
+  return __builtin_fabsf(x) < kTanhSeriesMax ? tanh_series(x) : tanh_exp_form(x);
 }
 
 // Online log-sum-exp / argmax state merge (running max m, sum of exp(z - m),
-// index of the first maximum).  Equal maxima keep the lower index.
+// index of the first maximum).  Equal maxima keep the lower index.  An empty
+// state is (-inf, 0, INT_MAX); the merge is branch-free and never forms
+// -inf - (-inf).
 __device__ __forceinline__ void merge_stats(float& m, float& s, int& a, float m2, float s2, int a2) {
-  if (m2 == kNegInf) return;
-  if (m == kNegInf) { m = m2; s = s2; a = a2; return; }
   const float M = __builtin_fmaxf(m, m2);
-  s = s * fast_exp(m - M) + s2 * fast_exp(m2 - M);
+  const float Mr = M == kNegInf ? 0.0f : M;
+  s = s * fast_exp(m - Mr) + s2 * fast_exp(m2 - Mr);
   a = (m > m2) ? a : (m2 > m) ? a2 : (a < a2 ? a : a2);
   m = M;
 }

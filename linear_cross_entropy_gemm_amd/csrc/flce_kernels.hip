@@ -23,37 +23,75 @@ namespace flce {
 // per 32 x 32 block and 16 of its vocabulary entries, so the row statistics
 // reduce in registers first, then across lanes l and l + 32, then across the
 // two waves that share the tokens.
-template <typename T>
+template <typename T, bool kCap>
 __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn,
                                              char* smem) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
   const int vbase = tm * kTile + wm * 128 + hi * 4;
+  const bool partial = tm * kTile + kTile > p.V;   // only the last vocabulary tile
+  const float scale = kCap ? p.mult * p.invT : p.mult;
   float best[4], sum[4];
   int bidx[4];
+  // One token block (bn) at a time, 64 values per lane.
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn) {
+    // z = T tanh(m a / T) (series for |x| < 1/4; the exponential form only
+    // when some lane needs it), or m a
+    bool need = false;
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[bm][bn][v] *= scale;
+        if (kCap) need |= __builtin_fabsf(acc[bm][bn][v]) >= kTanhSeriesMax;
+      }
+    if (kCap) {
+      if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[bm][bn][v] = p.T * softcap_tanh(acc[bm][bn][v]);
+      } else {
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[bm][bn][v] = p.T * tanh_series(acc[bm][bn][v]);
+      }
+    }
+    // padding columns take no part in the statistics (-inf; exp(-inf) = 0)
+    if (partial) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
+          acc[bm][bn][v] = col < p.V ? acc[bm][bn][v] : kNegInf;
+        }
+    }
     const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
     const bool tok_ok = tok < p.C_this;
-    const int64_t lab = tok_ok ? p.labels[tok] : INT64_MIN;
-    float mx = kNegInf;
+    const int64_t lab64 = tok_ok ? p.labels[tok] : -1;
+    const int lab = (lab64 >= 0 && lab64 < p.V) ? (int)lab64 : -1;
+    float mx = kNegInf, zl = 0.0f;
     int ax = 0x7fffffff;
+    bool found = false;
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
-        float x = acc[bm][bn][v] * p.mult;
-        if (p.T > 0.0f) x = p.T * softcap_tanh(x * p.invT);
-        acc[bm][bn][v] = x;
+        const float x = acc[bm][bn][v];
         // columns visit in increasing order: strict > keeps the first maximum
-        if (col < p.V && x > mx) {
-          mx = x;
-          ax = col;
-        }
-        if ((int64_t)col == lab) p.zlab[tok] = x;
+        const bool gt = x > mx;
+        mx = gt ? x : mx;
+        ax = gt ? col : ax;
+        const bool is_lab = col == lab;
+        zl = is_lab ? x : zl;
+        found |= is_lab;
       }
     }
+    if (found) p.zlab[tok] = zl;
     if (tok_ok) {
       T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + (int64_t)tok * p.ldz);
 #pragma unroll
@@ -64,15 +102,11 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
                  acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]);
     }
     float s = 0.0f;
-    if (mx != kNegInf) {
+    const float mref = mx == kNegInf ? 0.0f : mx;
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
-          if (col < p.V) s += fast_exp(acc[bm][bn][v] - mx);
-        }
-    }
+      for (int v = 0; v < 16; ++v) s += fast_exp(acc[bm][bn][v] - mref);
     const float m2 = __shfl_xor(mx, 32);
     const float s2 = __shfl_xor(s, 32);
     const int a2 = __shfl_xor(ax, 32);
@@ -112,7 +146,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
   const int64_t kbytes = (int64_t)p.H * Elem<T>::size;
@@ -129,7 +163,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
     lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0);
     gemm_mainloop<T>(la, lb, (int)((kbytes + kKBytes - 1) / kKBytes), smem, acc);
   }
-  fwd_epilogue<T>(acc, p, tm, tn, smem);
+  if (p.T > 0.0f)
+    fwd_epilogue<T, true>(acc, p, tm, tn, smem);
+  else
+    fwd_epilogue<T, false>(acc, p, tm, tn, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -208,7 +245,7 @@ __global__ __launch_bounds__(256) void grad_logits_kernel(GradLogitArgs p) {
 // contiguous, transposed through registers).
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
   const int k0 = sp * p.ksteps_per_split;
@@ -265,7 +302,7 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
 // block row in flight while the current one is added and stored.
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
   f32x16 acc[4][4];

@@ -411,13 +411,18 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
 // (64 bytes of K per operand row, 32 KiB per stage for A + B), loaded three K
 // steps ahead.
 //
+// The LDS serves 256 bytes (64 banks of 4 bytes) per cycle: a 16-byte read
+// instruction is serviced 16 lanes at a time and an 8-byte one 32 lanes at a
+// time, so the layouts below spread those lane groups over 16 distinct
+// 16-byte bank units.
+//
 // K-major operand stage (rows = M or N index, 4 chunks of 16 bytes of K per
-// row): rows 2L and 2L+1 share the 128-byte line L; chunk c of row r sits in
-// slot ((r & 1) * 4 + c) ^ (L & 7) of its line, so 8 consecutive rows reading
-// the same chunk hit 8 different bank groups.
+// row): rows 4B .. 4B+3 share the 256-byte bank row B; chunk c of row r sits
+// in unit ((r & 3) * 4 + c) ^ (B & 3), so 16 consecutive rows reading the same
+// chunk hit 16 different units.
 //
 // MN-major operand stage (rows = K index, 256 MN values = 512 bytes per row):
-// 16-byte unit u of row k sits at unit u ^ (2 (k & 3)).  A fragment is read
+// 16-byte unit u of row k sits at unit u ^ (4 (k & 3)).  A fragment is read
 // with two ds_read_b64_tr_b16: in each 16-lane group, lane p fetches 4
 // consecutive MN values of K row k0 + (p >> 2); the hardware hands lane p the
 // 4 K values of MN column (p) -- the same lane -> (row, K) assignment as a
@@ -426,7 +431,9 @@ constexpr int kDStages = 4;
 constexpr int kDKBytes = 64;
 constexpr int kDOperand = kTile * kDKBytes;   // 16 KiB
 constexpr int kDStage = 2 * kDOperand;        // 32 KiB
-static_assert(kDStages * kDStage == kLdsBytes, "LDS ring size");
+constexpr int kDLdsBytes = kDStages * kDStage;
+// loads in flight per wave behind the stage being waited for
+constexpr int kDWaitLoads = (kDStages - 2) * 8;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define FLCE_AS3 __attribute__((address_space(3)))
@@ -456,8 +463,8 @@ __device__ __forceinline__ void lds_dma16(const u32x4s& r, char* lds, uint32_t v
 }
 
 __device__ __forceinline__ int kd_offset(int r, int c) {
-  const int L = r >> 1;
-  return L * 128 + (((((r & 1) << 2) | c) ^ (L & 7)) << 4);
+  const int B = r >> 2;
+  return B * 256 + (((((r & 3) << 2) | c) ^ (B & 3)) << 4);
 }
 
 // K-major operand [mn][k] (k contiguous, row stride `ld` bytes).
@@ -479,9 +486,9 @@ struct KMajorDirect {
     k_bytes = k_bytes_;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int L = (4 * w + j) * 8 + (lam >> 3);
-      const int x = (lam & 7) ^ (L & 7);
-      const int r = 2 * L + (x >> 2), c = x & 3;
+      const int B = (4 * w + j) * 4 + (lam >> 4);
+      const int x = (lam & 15) ^ (B & 3);
+      const int r = 4 * B + (x >> 2), c = x & 3;
       voff[j] = r < rows ? (uint32_t)(r * ld + c * 16) : kOOB;
       c16[j] = c * 16;
     }
@@ -508,7 +515,7 @@ struct MNMajorDirect {
   int64_t ld;
   int krow0, k_valid;
   uint32_t voff[4];
-  int frag[2];   // per-lane offsets for even and odd blocks (sub-step 0, first half)
+  int frag[4];   // per-lane offsets of blocks 0..3 (sub-step 0, first half)
 
   __device__ __forceinline__ void init(const void* base_, int64_t ld_, int mn0, int mn_valid, int k_valid_,
                                        int kstep0, int row0, int lane) {
@@ -520,16 +527,17 @@ struct MNMajorDirect {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int kr = 8 * w + 2 * j + (lam >> 5);
-      const int u = (lam & 31) ^ ((kr & 3) << 1);
+      const int u = (lam & 31) ^ ((kr & 3) << 2);
       voff[j] = mn0 + 8 * u < mn_valid ? (uint32_t)(kr * ld + (int64_t)(mn0 + 8 * u) * 2) : kOOB;
     }
+    // lane (g, p): K row 8 (g >> 1) + (p >> 2) (+ 16 ks + 4 half), MN unit
+    // row0/8 + 4 b + 2 (g & 1) + ((p & 3) >> 1), byte (p & 1) * 8 of the unit
     const int g = lane >> 4, p = lane & 15;
-    const int f = (p >> 2) << 1;
+    const int q = p >> 2;
+    const int x = 2 * (g & 1) + ((p & 3) >> 1);
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int x = 2 * (g & 1) + ((p & 3) >> 1);
-      frag[par] = (8 * (g >> 1) + (p >> 2)) * 512 + ((((4 * par + x) ^ f)) << 4) + (p & 1) * 8 + row0 * 2;
-    }
+    for (int b = 0; b < 4; ++b)
+      frag[b] = (8 * (g >> 1) + q) * 512 + (((4 * b + x) ^ (4 * q)) << 4) + (p & 1) * 8 + row0 * 2;
   }
   __device__ __forceinline__ void issue_part(char* stage, int j) {
     const u32x4s rs = make_rsrc_words(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
@@ -537,7 +545,7 @@ struct MNMajorDirect {
   }
   __device__ __forceinline__ void advance() { krow0 += 32; }
   __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
-    const char* q = stage + frag[b & 1] + ks * 8192 + (b >> 1) * 128;
+    const char* q = stage + frag[b] + ks * 8192;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLCE_AS3 i16x4*)(q));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLCE_AS3 i16x4*)(q + 4 * 512));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -554,7 +562,7 @@ struct MNMajorDirect {
 
 // K loop of the direct-to-LDS pipeline.  Per K step (2 sub-steps of 16 MFMAs
 // per wave): sub-step 0 runs while the fragments of sub-step 1 are read and
-// the 8 loads three steps ahead are issued; then the wave waits for the next
+// the 8 loads kDStages - 1 steps ahead are issued; then the wave waits for the next
 // stage's loads, and the barrier both publishes that stage and frees the one
 // just read; sub-step 1 runs while sub-step 0 of the next stage is read.
 template <class LA, class LB>
@@ -575,7 +583,7 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
     la.advance();
     lb.advance();
   }
-  FLCE_WAIT_VMCNT(16);
+  FLCE_WAIT_VMCNT(kDWaitLoads);
   __syncthreads();
   u32x4 a[2][4], b[2][4];
 #pragma unroll
@@ -583,10 +591,11 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
     b[0][i] = lb.read(smem + kDOperand, i, 0);
     a[0][i] = la.read(smem, i, 0);
   }
+  static_assert((kDStages & (kDStages - 1)) == 0, "ring slots use a power-of-two mask");
   for (int it = 0; it < nk; ++it) {
-    const char* cur = smem + (it & 3) * kDStage;
-    const char* nxt = smem + ((it + 1) & 3) * kDStage;
-    char* dst = smem + ((it + 3) & 3) * kDStage;
+    const char* cur = smem + (it & (kDStages - 1)) * kDStage;
+    const char* nxt = smem + ((it + 1) & (kDStages - 1)) * kDStage;
+    char* dst = smem + ((it + kDStages - 1) & (kDStages - 1)) * kDStage;
     // sub-step 0 (+ reads of sub-step 1, + loads for step it + 3)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -607,7 +616,7 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
     la.advance();
     lb.advance();
     FLCE_FENCE();
-    FLCE_WAIT_VMCNT_LDS(16);
+    FLCE_WAIT_VMCNT_LDS(kDWaitLoads);
     __syncthreads();
     FLCE_FENCE();
     // sub-step 1 (+ reads of sub-step 0 of the next stage)
