@@ -15,6 +15,9 @@ sample of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -41,6 +44,78 @@ WORKLOAD_TEXT = {
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "linear_cross_entropy_gemm_amd", "csrc")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: a traffic figure measured on other sources is stale."""
+    m = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        m.update(os.path.basename(f).encode())
+        m.update(open(f, "rb").read())
+    return m.hexdigest()[:16]
+
+
+def copy_calibration() -> int:
+    """A plain device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES),
+    three times: the reference the FETCH_SIZE / WRITE_SIZE counters are
+    scaled by."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {COPY_BYTES} bytes x3")
+    return 0
+
+
+def _pmc_per_dispatch(d: str, counter: str, name_part: str) -> list:
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def summarize_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                      copy_write_dir: str, out: str, command: str) -> int:
+    """Turn four rocprofv3 --pmc runs into HBM bytes per launch of `kernel`."""
+    cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copy")
+    cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", "copy")
+    kf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
+    kw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    if not (cf and cw and kf and kw):
+        log("[bench] missing counter values")
+        return 1
+    # counters read in KiB; the factor maps them onto the copy's known bytes
+    f_scale = COPY_BYTES / (max(cf) * 1024.0)
+    w_scale = COPY_BYTES / (max(cw) * 1024.0)
+    fetch = sum(kf) / len(kf) * 1024.0 * f_scale
+    write = sum(kw) / len(kw) * 1024.0 * w_scale
+    rec = {"kernel": kernel, "source_hash": kernel_source_hash(), "launches": len(kf),
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write,
+           "copy_fetch_kib": max(cf), "copy_write_kib": max(cw), "fetch_scale": f_scale, "write_scale": w_scale,
+           "command": command}
+    json.dump(rec, open(out, "w"), indent=1)
+    log(f"[bench] {kernel}: fetch {fetch / 1e9:.3f} GB + write {write / 1e9:.3f} GB per launch -> {out}")
+    return 0
+
+
+def stored_traffic(kernel: str, config: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{config}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def blas_threads() -> int:
@@ -78,9 +153,19 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c4", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--cpu-tokens", type=int, default=512)
+    ap.add_argument("--cpu-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=6,
+                    metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
+                    help="write HBM traffic per launch from four rocprofv3 --pmc runs")
+    ap.add_argument("--command", default="", help="command text recorded with --summarize-traffic")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.summarize_traffic:
+        return summarize_traffic(*args.summarize_traffic, command=args.command)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not part of this build", file=sys.stderr)
@@ -155,8 +240,9 @@ def main() -> int:
     dom = max((k for k in kernels if k in GEMM_KINDS), key=lambda k: kernels[k]["ms_per_step"])
     flops_per_launch = 2.0 * cfg.N * cfg.H * cfg.V / kernels[dom]["launches_per_step"]
     achieved = flops_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+    traffic = stored_traffic(dom, args.config)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                 "flops_per_launch": flops_per_launch, "avg_launch_ms": round(kernels[dom]["avg_ms"], 4)}
 
     result = {

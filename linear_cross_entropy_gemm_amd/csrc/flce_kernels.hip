@@ -253,13 +253,14 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
   const int nk = rem < p.ksteps_per_split ? rem : p.ksteps_per_split;
   f32x16 acc[4][4];
   if constexpr (sizeof(T) == 2) {
-    // the split is planned in 128-byte K steps; the direct pipeline runs 64-byte steps
+    // the split is planned in 128-byte K steps; the direct pipeline runs kDKBytes steps
+    constexpr int r = kKBytes / kDKBytes;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     KMajorDirect la;
-    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, 2 * k0, (wave >> 1) * 128, lane);
+    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, r * k0, (wave >> 1) * 128, lane);
     MNMajorDirect lb;
-    lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, 2 * k0, (wave & 1) * 128, lane);
-    gemm_mainloop_direct(la, lb, 2 * nk, smem, acc);
+    lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, r * k0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, r * nk, smem, acc);
   } else {
     KMajorLoader la;
     la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * Elem<T>::size, k0);
@@ -311,7 +312,8 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
     MNMajorDirect la, lb;
     la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0, (wave >> 1) * 128, lane);
     lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0, (wave & 1) * 128, lane);
-    gemm_mainloop_direct(la, lb, (p.C_this + 31) / 32, smem, acc);
+    constexpr int bk = kDKBytes / 2;
+    gemm_mainloop_direct(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
   } else {
     MNMajorLoader<T> la, lb;
     la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);

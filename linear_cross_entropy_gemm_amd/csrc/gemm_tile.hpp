@@ -407,19 +407,19 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
 // Global tiles go straight into LDS with buffer_load_dwordx4 ... lds (lane l
 // of an instruction fills the 16 bytes at M0 + 16 l; out-of-range offsets
 // fill zeros), so no registers stage the operands and no LDS store
-// instructions are issued.  The LDS holds a ring of 4 stages of 32 K
-// (64 bytes of K per operand row, 32 KiB per stage for A + B), loaded three K
-// steps ahead.
+// instructions are issued.  The LDS holds a ring of kDStages stages of
+// kDKBytes bytes of K per operand row, loaded kDStages - 1 K steps ahead.
 //
 // The LDS serves 256 bytes (64 banks of 4 bytes) per cycle: a 16-byte read
 // instruction is serviced 16 lanes at a time and an 8-byte one 32 lanes at a
 // time, so the layouts below spread those lane groups over 16 distinct
 // 16-byte bank units.
 //
-// K-major operand stage (rows = M or N index, 4 chunks of 16 bytes of K per
-// row): rows 4B .. 4B+3 share the 256-byte bank row B; chunk c of row r sits
-// in unit ((r & 3) * 4 + c) ^ (B & 3), so 16 consecutive rows reading the same
-// chunk hit 16 different units.
+// K-major operand stage (rows = M or N index, kDCpr chunks of 16 bytes of K
+// per row): the kDRpb rows r of one 256-byte bank row B = r / kDRpb hold
+// chunk c at unit ((r % kDRpb) * kDCpr + c) ^ (B % kDCpr), so 16 consecutive
+// rows reading the same chunk hit 16 different units.  Each load instruction
+// covers whole 128-byte row pieces when kDKBytes = 128.
 //
 // MN-major operand stage (rows = K index, 256 MN values = 512 bytes per row):
 // 16-byte unit u of row k sits at unit u ^ (4 (k & 3)).  A fragment is read
@@ -427,13 +427,19 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
 // consecutive MN values of K row k0 + (p >> 2); the hardware hands lane p the
 // 4 K values of MN column (p) -- the same lane -> (row, K) assignment as a
 // K-major 16-byte fragment read.
+constexpr int kDKBytes = 64;                    // K bytes per row per stage (32 bf16)
 constexpr int kDStages = 4;
-constexpr int kDKBytes = 64;
-constexpr int kDOperand = kTile * kDKBytes;   // 16 KiB
-constexpr int kDStage = 2 * kDOperand;        // 32 KiB
+constexpr int kDSub = kDKBytes / 32;            // 16-wide MFMA sub-steps per K step
+constexpr int kDCpr = kDKBytes / 16;            // chunks per K-major row
+constexpr int kDRpb = 256 / kDKBytes;           // K-major rows per 256-byte bank row
+constexpr int kDLoads = kDKBytes / 16;          // load instructions per wave per operand per stage
+constexpr int kDOperand = kTile * kDKBytes;
+constexpr int kDStage = 2 * kDOperand;
 constexpr int kDLdsBytes = kDStages * kDStage;
 // loads in flight per wave behind the stage being waited for
-constexpr int kDWaitLoads = (kDStages - 2) * 8;
+constexpr int kDWaitLoads = (kDStages - 2) * 2 * kDLoads;
+static_assert(kDLdsBytes <= 160 * 1024, "LDS capacity");
+static_assert((kDStages & (kDStages - 1)) == 0, "ring slots use a power-of-two mask");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define FLCE_AS3 __attribute__((address_space(3)))
@@ -463,17 +469,17 @@ __device__ __forceinline__ void lds_dma16(const u32x4s& r, char* lds, uint32_t v
 }
 
 __device__ __forceinline__ int kd_offset(int r, int c) {
-  const int B = r >> 2;
-  return B * 256 + (((((r & 3) << 2) | c) ^ (B & 3)) << 4);
+  const int B = r / kDRpb;
+  return B * 256 + ((((r % kDRpb) * kDCpr + c) ^ (B % kDCpr)) << 4);
 }
 
 // K-major operand [mn][k] (k contiguous, row stride `ld` bytes).
 struct KMajorDirect {
   const char* base;
   int64_t range0, kpos, k_bytes;
-  uint32_t voff[4];
-  int c16[4];
-  int frag[2];   // per-lane fragment offsets for sub-steps 0 and 1 (block 0)
+  uint32_t voff[kDLoads];
+  int c16[kDLoads];
+  int frag[kDSub];   // per-lane fragment offsets of block 0 per sub-step
 
   __device__ __forceinline__ void init(const void* base_, int64_t ld, int mn0, int mn_valid, int64_t k_bytes_,
                                        int kstep0, int row0, int lane) {
@@ -485,27 +491,27 @@ struct KMajorDirect {
     kpos = (int64_t)kstep0 * kDKBytes;
     k_bytes = k_bytes_;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int B = (4 * w + j) * 4 + (lam >> 4);
-      const int x = (lam & 15) ^ (B & 3);
-      const int r = 4 * B + (x >> 2), c = x & 3;
+    for (int j = 0; j < kDLoads; ++j) {
+      const int B = (w * kDLoads + j) * 4 + (lam >> 4);
+      const int x = (lam & 15) ^ (B % kDCpr);
+      const int r = B * kDRpb + x / kDCpr, c = x % kDCpr;
       voff[j] = r < rows ? (uint32_t)(r * ld + c * 16) : kOOB;
       c16[j] = c * 16;
     }
     const int lo = lane & 31, hi = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) frag[ks] = kd_offset(row0 + lo, 2 * ks + hi);
+    for (int ks = 0; ks < kDSub; ++ks) frag[ks] = kd_offset(row0 + lo, 2 * ks + hi);
   }
-  // Issue this wave's 4 loads of the next K step into `stage` (16 KiB).
+  // Issue this wave's load j of the current K step into `stage`.
   __device__ __forceinline__ void issue_part(char* stage, int j) {
     const u32x4s rs = make_rsrc_words(base + kpos, range0 - kpos);
     const uint32_t off = kpos + c16[j] < k_bytes ? voff[j] : kOOB;
-    lds_dma16(rs, stage + ((threadIdx.x >> 6) * 4 + j) * 1024, off);
+    lds_dma16(rs, stage + ((threadIdx.x >> 6) * kDLoads + j) * 1024, off);
   }
   __device__ __forceinline__ void advance() { kpos += kDKBytes; }
   // Fragment of block b (rows row0 + 32 b + (l & 31)) for sub-step ks.
   __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
-    return *reinterpret_cast<const u32x4*>(stage + frag[ks] + b * 2048);
+    return *reinterpret_cast<const u32x4*>(stage + frag[ks] + b * 32 * kDKBytes);
   }
 };
 
@@ -514,7 +520,7 @@ struct MNMajorDirect {
   const char* base;
   int64_t ld;
   int krow0, k_valid;
-  uint32_t voff[4];
+  uint32_t voff[kDLoads];
   int frag[4];   // per-lane offsets of blocks 0..3 (sub-step 0, first half)
 
   __device__ __forceinline__ void init(const void* base_, int64_t ld_, int mn0, int mn_valid, int k_valid_,
@@ -522,11 +528,11 @@ struct MNMajorDirect {
     const int t = threadIdx.x, w = t >> 6, lam = t & 63;
     ld = ld_;
     base = static_cast<const char*>(base_);
-    krow0 = kstep0 * 32;
+    krow0 = kstep0 * (kDKBytes / 2);
     k_valid = k_valid_;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kr = 8 * w + 2 * j + (lam >> 5);
+    for (int j = 0; j < kDLoads; ++j) {
+      const int kr = (w * kDLoads + j) * 2 + (lam >> 5);
       const int u = (lam & 31) ^ ((kr & 3) << 2);
       voff[j] = mn0 + 8 * u < mn_valid ? (uint32_t)(kr * ld + (int64_t)(mn0 + 8 * u) * 2) : kOOB;
     }
@@ -541,9 +547,9 @@ struct MNMajorDirect {
   }
   __device__ __forceinline__ void issue_part(char* stage, int j) {
     const u32x4s rs = make_rsrc_words(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
-    lds_dma16(rs, stage + ((threadIdx.x >> 6) * 4 + j) * 1024, voff[j]);
+    lds_dma16(rs, stage + ((threadIdx.x >> 6) * kDLoads + j) * 1024, voff[j]);
   }
-  __device__ __forceinline__ void advance() { krow0 += 32; }
+  __device__ __forceinline__ void advance() { krow0 += kDKBytes / 2; }
   __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
     const char* q = stage + frag[b] + ks * 8192;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLCE_AS3 i16x4*)(q));
@@ -560,11 +566,22 @@ struct MNMajorDirect {
 // after which other waves refill the stage this wave has just read.
 #define FLCE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
 
-// K loop of the direct-to-LDS pipeline.  Per K step (2 sub-steps of 16 MFMAs
-// per wave): sub-step 0 runs while the fragments of sub-step 1 are read and
-// the 8 loads kDStages - 1 steps ahead are issued; then the wave waits for the next
-// stage's loads, and the barrier both publishes that stage and frees the one
-// just read; sub-step 1 runs while sub-step 0 of the next stage is read.
+template <class LA, class LB>
+__device__ __forceinline__ void issue_loads(LA& la, LB& lb, char* stage, int idx) {
+  if (idx < kDLoads)
+    la.issue_part(stage, idx);
+  else
+    lb.issue_part(stage + kDOperand, idx - kDLoads);
+}
+
+// K loop of the direct-to-LDS pipeline.  Per K step, kDSub sub-steps of 16
+// MFMAs per wave, each split into 4 block-row groups fenced in program order;
+// alongside each group the next sub-step's fragments are read (B first).  The
+// 2 * kDLoads loads for kDStages - 1 steps ahead are spread over the groups of
+// the first half of the step.  Before the last sub-step the wave waits for the
+// next stage's loads and its own LDS reads, and the barrier both publishes
+// that stage and frees the one just read; the last sub-step then runs while
+// sub-step 0 of the next stage is read.
 template <class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
 #pragma unroll
@@ -577,59 +594,54 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
 #pragma unroll
   for (int s = 0; s < kDStages - 1; ++s) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) la.issue_part(smem + s * kDStage, j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lb.issue_part(smem + s * kDStage + kDOperand, j);
+    for (int i = 0; i < 2 * kDLoads; ++i) issue_loads(la, lb, smem + s * kDStage, i);
     la.advance();
     lb.advance();
   }
   FLCE_WAIT_VMCNT(kDWaitLoads);
   __syncthreads();
+  constexpr int kLoadGroups = kDSub / 2 * 4;             // groups that issue loads
+  constexpr int kPerGroup = 2 * kDLoads / kLoadGroups;   // loads per such group
+  static_assert(kPerGroup * kLoadGroups == 2 * kDLoads, "even load spread");
   u32x4 a[2][4], b[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     b[0][i] = lb.read(smem + kDOperand, i, 0);
     a[0][i] = la.read(smem, i, 0);
   }
-  static_assert((kDStages & (kDStages - 1)) == 0, "ring slots use a power-of-two mask");
   for (int it = 0; it < nk; ++it) {
     const char* cur = smem + (it & (kDStages - 1)) * kDStage;
     const char* nxt = smem + ((it + 1) & (kDStages - 1)) * kDStage;
     char* dst = smem + ((it + kDStages - 1) & (kDStages - 1)) * kDStage;
-    // sub-step 0 (+ reads of sub-step 1, + loads for step it + 3)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      FLCE_FENCE();
-      mma_row(acc, a[0][g], b[0], g, bf16{});
-      if (g < 2) {
-        b[1][2 * g] = lb.read(cur + kDOperand, 2 * g, 1);
-        b[1][2 * g + 1] = lb.read(cur + kDOperand, 2 * g + 1, 1);
-        la.issue_part(dst, 2 * g);
-        la.issue_part(dst, 2 * g + 1);
-      } else {
-        a[1][2 * g - 4] = la.read(cur, 2 * g - 4, 1);
-        a[1][2 * g - 3] = la.read(cur, 2 * g - 3, 1);
-        lb.issue_part(dst + kDOperand, 2 * g - 4);
-        lb.issue_part(dst + kDOperand, 2 * g - 3);
+    for (int ks = 0; ks < kDSub; ++ks) {
+      const int p = ks & 1, q = p ^ 1;
+      const bool last = ks == kDSub - 1;
+      if (last) {
+        la.advance();
+        lb.advance();
+        FLCE_FENCE();
+        FLCE_WAIT_VMCNT_LDS(kDWaitLoads);
+        __syncthreads();
+        FLCE_FENCE();
       }
-    }
-    la.advance();
-    lb.advance();
-    FLCE_FENCE();
-    FLCE_WAIT_VMCNT_LDS(kDWaitLoads);
-    __syncthreads();
-    FLCE_FENCE();
-    // sub-step 1 (+ reads of sub-step 0 of the next stage)
+      const char* src = last ? nxt : cur;
+      const int nks = last ? 0 : ks + 1;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      FLCE_FENCE();
-      mma_row(acc, a[1][g], b[1], g, bf16{});
-      if (g < 2) {
-        b[0][2 * g] = lb.read(nxt + kDOperand, 2 * g, 0);
-        b[0][2 * g + 1] = lb.read(nxt + kDOperand, 2 * g + 1, 0);
-      } else {
-        a[0][2 * g - 4] = la.read(nxt, 2 * g - 4, 0);
-        a[0][2 * g - 3] = la.read(nxt, 2 * g - 3, 0);
+      for (int g = 0; g < 4; ++g) {
+        FLCE_FENCE();
+        mma_row(acc, a[p][g], b[p], g, bf16{});
+        if (g < 2) {
+          b[q][2 * g] = lb.read(src + kDOperand, 2 * g, nks);
+          b[q][2 * g + 1] = lb.read(src + kDOperand, 2 * g + 1, nks);
+        } else {
+          a[q][2 * g - 4] = la.read(src, 2 * g - 4, nks);
+          a[q][2 * g - 3] = la.read(src, 2 * g - 3, nks);
+        }
+        if (ks < kDSub / 2) {
+#pragma unroll
+          for (int i = 0; i < kPerGroup; ++i) issue_loads(la, lb, dst, (ks * 4 + g) * kPerGroup + i);
+        }
       }
     }
   }
