@@ -55,7 +55,7 @@ enum {
   FLCE_EWORKSPACE = 2,    /* workspace smaller than flce_workspace_size() for the call */
   FLCE_EDEVICE = 3,       /* a HIP launch or runtime call failed */
   FLCE_ELABEL = 4,        /* (device-detected) a label outside [0, V) that is not ignore_index */
-  FLCE_EUNSUPPORTED = 5   /* valid but unsupported shape, e.g. H not a multiple of 8 (bf16) / 4 (fp32) */
+  FLCE_EUNSUPPORTED = 5   /* valid but unsupported shape, e.g. H not a multiple of 8 (bf16) / 4 (fp32) or too large */
 };
 
 /*
@@ -79,7 +79,8 @@ typedef struct {
  * `budget_bytes` of workspace (0 = default budget of 16 GiB).  Pure host
  * arithmetic; no GPU needed.  Returns FLCE_OK, FLCE_EINVAL (negative sizes,
  * bad dtype, null `out`), FLCE_EUNSUPPORTED (H not a multiple of 8 for bf16 or
- * 4 for fp32) or FLCE_EWORKSPACE (not even the smallest chunk fits).
+ * 4 for fp32; H > 2^21; V above 2^22 - 256 for bf16 or 2^21 - 256 for fp32;
+ * N >= 2^31) or FLCE_EWORKSPACE (not even the smallest chunk fits).
  */
 int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget_bytes, flce_plan_t* out);
 

@@ -85,7 +85,7 @@ extern "C" const char* flce_strerror(int code) {
     case FLCE_EWORKSPACE: return "workspace too small for any chunk plan";
     case FLCE_EDEVICE: return "HIP launch or runtime call failed";
     case FLCE_ELABEL: return "a label outside [0, V) that is not ignore_index";
-    case FLCE_EUNSUPPORTED: return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32)";
+    case FLCE_EUNSUPPORTED: return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32; H <= 2^21; V <= 2^22 - 256 for bf16, 2^21 - 256 for fp32)";
     default: return "unknown error code";
   }
 }

@@ -151,6 +151,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
   map_tile(p.map, tm, tn, sp);
   const int64_t kbytes = (int64_t)p.H * Elem<T>::size;
   f32x16 acc[4][4];
+  zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     KMajorDirect la, lb;
@@ -252,6 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
   const int rem = p.ksteps_total - k0;
   const int nk = rem < p.ksteps_per_split ? rem : p.ksteps_per_split;
   f32x16 acc[4][4];
+  zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
     // the split is planned in 128-byte K steps; the direct pipeline runs kDKBytes steps
     constexpr int r = kKBytes / kDKBytes;
@@ -299,21 +301,54 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
 // slow dimension and are transposed through registers.  With hidden on the M
 // side each lane owns 4 consecutive hidden entries of one vocabulary row of
 // grad_W per accumulator group, so the fp32 epilogue moves 16 bytes per
-// access; the read-modify-write of later chunks keeps the loads of the next
-// block row in flight while the current one is added and stored.
-template <typename T>
+// access.  For every chunk after the first (kAccumulate) the accumulators
+// start from the stored grad_W instead of zero, so the epilogue only stores.
+template <typename T, bool kAccumulate>
 __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
+  // accumulator element (bm, bn, 4 i .. 4 i + 3): vocabulary row
+  // n0 + 32 bn, hidden entries m0 + 32 bm + 8 i .. + 3; with m a multiple of
+  // 4 and H a multiple of 4, m < H keeps the whole vector inside the row
+  const int n0 = tn * kTile + wn * 128 + lo;
+  const int m0 = tm * kTile + wm * 128 + 4 * hi;
+  auto vec_ok = [&](int bm, int bn, int i) { return n0 + bn * 32 < p.V && m0 + bm * 32 + 8 * i < p.H; };
+  // byte offset of vector (bm, bn, i) from the tile's first element
+  auto voff = [&](int bm, int bn, int i) -> uint32_t {
+    return (uint32_t)((((int64_t)(wn * 128 + lo + bn * 32) * p.H) + wm * 128 + 4 * hi + bm * 32 + 8 * i) * 4);
+  };
+  float* tile0 = p.gW + (int64_t)tn * kTile * p.H + (int64_t)tm * kTile;
   f32x16 acc[4][4];
+  if constexpr (kAccumulate) {
+    // The products are added onto the grad_W accumulated so far: its loads
+    // are issued before the first K stages, so they overlap the pipeline fill
+    // instead of stalling the epilogue.  Vectors outside the matrix read as 0.
+    const int64_t rows = (int64_t)(p.V - tn * kTile < kTile ? p.V - tn * kTile : kTile);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)tile0, (rows * p.H - (int64_t)tm * kTile) * 4);
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 o = __builtin_bit_cast(f32x4, load16(rs, vec_ok(bm, bn, i) ? voff(bm, bn, i) : kOOB));
+          acc[bm][bn][4 * i] = o[0];
+          acc[bm][bn][4 * i + 1] = o[1];
+          acc[bm][bn][4 * i + 2] = o[2];
+          acc[bm][bn][4 * i + 3] = o[3];
+        }
+  } else {
+    zero_acc(acc);
+  }
   if constexpr (sizeof(T) == 2) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     MNMajorDirect la, lb;
-    la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0, (wave >> 1) * 128, lane);
-    lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0, (wave & 1) * 128, lane);
+    la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0, wm * 128, lane);
+    lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0, wn * 128, lane);
     constexpr int bk = kDKBytes / 2;
-    gemm_mainloop_direct(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
+    gemm_mainloop_direct<kAccumulate>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
   } else {
     MNMajorLoader<T> la, lb;
     la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);
@@ -321,55 +356,15 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
     constexpr int bk = kKBytes / Elem<T>::size;
     gemm_mainloop<T>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
-  // element (bm, bn, i): vocabulary row n, hidden entries m .. m + 3
-  const int n0 = tn * kTile + wn * 128 + lo;
-  const int m0 = tm * kTile + wm * 128 + 4 * hi;
-  auto ptr = [&](int bm, int bn, int i) -> f32x4* {
-    return reinterpret_cast<f32x4*>(p.gW + (int64_t)(n0 + bn * 32) * p.H + m0 + bm * 32 + 8 * i);
-  };
-  // vector (bm, bn, i) covers hidden m .. m + 3 with m a multiple of 4 and
-  // H a multiple of 4, so m < H keeps the whole vector inside the row
-  auto vec_ok = [&](int bm, int bn, int i) { return n0 + bn * 32 < p.V && m0 + bm * 32 + 8 * i < p.H; };
-  if (!p.accumulate) {
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (vec_ok(bm, bn, i))
-            *ptr(bm, bn, i) = f32x4{acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1], acc[bm][bn][4 * i + 2],
-                                    acc[bm][bn][4 * i + 3]};
-    return;
-  }
-  f32x4 old[2][16];
-#pragma unroll
-  for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      old[0][bn * 4 + i] = vec_ok(0, bn, i) ? *ptr(0, bn, i) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
-    const int cb = bm & 1;
-    if (bm + 1 < 4) {
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          old[cb ^ 1][bn * 4 + i] = vec_ok(bm + 1, bn, i) ? *ptr(bm + 1, bn, i) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (vec_ok(bm, bn, i)) {
-          const f32x4 o = old[cb][bn * 4 + i];
-          *ptr(bm, bn, i) = f32x4{o[0] + acc[bm][bn][4 * i], o[1] + acc[bm][bn][4 * i + 1],
-                                  o[2] + acc[bm][bn][4 * i + 2], o[3] + acc[bm][bn][4 * i + 3]};
-        }
-  }
+        if (vec_ok(bm, bn, i))
+          *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(tile0) + voff(bm, bn, i)) =
+              f32x4{acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1], acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -555,7 +550,10 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gw.map = TileMap{tiles_hid, tiles_voc, 1, 4, 1, 1};
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_W, st);
-      grad_W_kernel<T><<<tiles_hid * tiles_voc, kThreads, 0, st>>>(gw);
+      if (gw.accumulate)
+        grad_W_kernel<T, true><<<tiles_hid * tiles_voc, kThreads, 0, st>>>(gw);
+      else
+        grad_W_kernel<T, false><<<tiles_hid * tiles_voc, kThreads, 0, st>>>(gw);
     }
   }
   FinalizeArgs fa;

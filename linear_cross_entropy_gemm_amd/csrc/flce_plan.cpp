@@ -74,9 +74,12 @@ int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* o
   if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
   const int64_t es = dtype == FLCE_DTYPE_BF16 ? 2 : 4;
   if ((H * es) % 16 != 0) return FLCE_EUNSUPPORTED;
-  // 32-bit indices inside the kernels
-  if (N > (int64_t(1) << 31) - 1 || H > (int64_t(1) << 24) || V > (int64_t(1) << 30))
-    return FLCE_EUNSUPPORTED;
+  // The GEMM loaders address a 256-row tile of an operand or of grad_W
+  // (fp32) with 32-bit byte offsets: 256 rows of H or Vp elements must stay
+  // within 2^31 bytes.
+  const int64_t lim_h = (int64_t(1) << 31) / (int64_t(kRowTile) * 4);
+  const int64_t lim_v = (int64_t(1) << 31) / (int64_t(kRowTile) * es) - kVocabTile;
+  if (N > (int64_t(1) << 31) - 1 || H > lim_h || V > lim_v) return FLCE_EUNSUPPORTED;
   if (budget == 0) budget = kDefaultBudget;
 
   Plan p{};

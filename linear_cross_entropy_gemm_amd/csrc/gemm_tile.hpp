@@ -77,6 +77,15 @@ __device__ __forceinline__ void map_tile(const TileMap& t, int& tm, int& tn, int
   tn = t.swap_walk ? a : b;
 }
 
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[bm][bn][v] = 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Global loads are raw buffer loads: a descriptor (base, byte range) lives in
 // scalar registers and each lane supplies a byte offset.  Offsets at or past
@@ -322,19 +331,14 @@ __device__ __forceinline__ u32x4 lds_read16(const char* stage, int off) {
 //   sub-step 3: its fragments come from registers; read sub-step 0 of the
 //               next stage.
 // Fetches and stores run every step (past the last K step the loads are out
-// of range and read zeros).  Ends with a barrier, after which the LDS may be
-// reused by the epilogue.
+// of range and read zeros).  The products are added to the values `acc`
+// holds on entry.  Ends with a barrier, after which the LDS may be reused by
+// the epilogue.
 template <typename T, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   FragAddr fa;
   fa.init(wave >> 1, wave & 1, lane);
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[bm][bn][v] = 0.0f;
   if (nk <= 0) return;
   la.fetch();
   lb.fetch();
@@ -581,15 +585,23 @@ __device__ __forceinline__ void issue_loads(LA& la, LB& lb, char* stage, int idx
 // the first half of the step.  Before the last sub-step the wave waits for the
 // next stage's loads and its own LDS reads, and the barrier both publishes
 // that stage and frees the one just read; the last sub-step then runs while
-// sub-step 0 of the next stage is read.
-template <class LA, class LB>
+// sub-step 0 of the next stage is read.  The products are added to the
+// values `acc` holds on entry; kLoadedAcc says that those were loaded from
+// memory just before the call.
+// Marks every accumulator as used here.  When the accumulators were loaded
+// from memory, the compiler's own wait for those loads lands on this point
+// (where it costs one wait per tile) instead of on the first MFMA inside the
+// K loop, where it would drain the load pipeline every step.
+__device__ __forceinline__ void touch_acc(f32x16 (&acc)[4][4]) {
+  asm volatile(""
+               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
+                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
+                 "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
+                 "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
+}
+
+template <bool kLoadedAcc = false, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[bm][bn][v] = 0.0f;
   if (nk <= 0) return;
 #pragma unroll
   for (int s = 0; s < kDStages - 1; ++s) {
@@ -600,6 +612,7 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
   }
   FLCE_WAIT_VMCNT(kDWaitLoads);
   __syncthreads();
+  if constexpr (kLoadedAcc) touch_acc(acc);
   constexpr int kLoadGroups = kDSub / 2 * 4;             // groups that issue loads
   constexpr int kPerGroup = 2 * kDLoads / kLoadGroups;   // loads per such group
   static_assert(kPerGroup * kLoadGroups == 2 * kDLoads, "even load spread");

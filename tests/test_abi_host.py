@@ -79,11 +79,21 @@ def test_plan_small_and_degenerate():
 def test_plan_rejects():
     for args, code in [((-1, 8, 8, 0), L.FLCE_EINVAL), ((4, 0, 8, 0), L.FLCE_EINVAL),
                        ((4, 8, 0, 0), L.FLCE_EINVAL), ((4, 8, 8, 7), L.FLCE_EINVAL),
-                       ((4, 12, 8, 0), L.FLCE_EUNSUPPORTED), ((4, 6, 8, 1), L.FLCE_EUNSUPPORTED)]:
+                       ((4, 12, 8, 0), L.FLCE_EUNSUPPORTED), ((4, 6, 8, 1), L.FLCE_EUNSUPPORTED),
+                       # 256-row tiles are addressed with 32-bit byte offsets
+                       ((4, 2 ** 21 + 8, 8, 0), L.FLCE_EUNSUPPORTED),
+                       ((4, 8, 2 ** 22 - 255, 0), L.FLCE_EUNSUPPORTED),
+                       ((4, 8, 2 ** 21 - 255, 1), L.FLCE_EUNSUPPORTED)]:
         with pytest.raises(L.FlceError) as e:
             L.flce_plan(*args)
         assert e.value.code == code, args
         assert L.flce_workspace_size(*args) == 0
+
+
+def test_plan_accepts_the_largest_shapes():
+    for args in [(4, 2 ** 21, 8, 0), (4, 8, 2 ** 22 - 256, 0), (4, 8, 2 ** 21 - 256, 1)]:
+        p = L.flce_plan(*args, budget_bytes=1 << 40)
+        assert p.vocab_padded >= args[2]
 
 
 def test_accumulator_sizes_match_the_pages():
