@@ -255,14 +255,14 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
   f32x16 acc[4][4];
   zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
-    // the split is planned in 128-byte K steps; the direct pipeline runs kDKBytes steps
-    constexpr int r = kKBytes / kDKBytes;
+    // the split is planned in 128-byte K steps, the direct pipeline's step
+    static_assert(kKBytes == kDKBytes, "one K step per planned step");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     KMajorDirect la;
-    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, r * k0, (wave >> 1) * 128, lane);
+    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, k0, (wave >> 1) * 128, lane);
     MNMajorDirect lb;
-    lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, r * k0, (wave & 1) * 128, lane);
-    gemm_mainloop_direct(la, lb, r * nk, smem, acc);
+    lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, nk, smem, acc);
   } else {
     KMajorLoader la;
     la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * Elem<T>::size, k0);

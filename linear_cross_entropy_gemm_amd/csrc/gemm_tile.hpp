@@ -411,39 +411,43 @@ __device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* smem
 // Global tiles go straight into LDS with buffer_load_dwordx4 ... lds (lane l
 // of an instruction fills the 16 bytes at M0 + 16 l; out-of-range offsets
 // fill zeros), so no registers stage the operands and no LDS store
-// instructions are issued.  The LDS holds a ring of kDStages stages of
-// kDKBytes bytes of K per operand row, loaded kDStages - 1 K steps ahead.
+// instructions are issued.  A K step moves 128 bytes of K per operand row, so
+// every request of a K-major operand is a whole 128-byte line; the load path
+// sustains far more bandwidth with whole-line requests than with half lines.
+//
+// The LDS holds a ring of five operand slots of 32 KB (one operand's 256 rows
+// for one K step; 160 KB in all).  Step t computes from A_t and B_t; A_{t+1},
+// B_{t+1} and A_{t+2} are in flight or landed, and the slots of A_t and B_t
+// are refilled once the step's barrier has released them.  With A_t in slot
+// 2t mod 5 and B_t in slot 2t + 1 mod 5, B_{t+2} goes to A_t's slot and A_{t+3}
+// to B_t's.
 //
 // The LDS serves 256 bytes (64 banks of 4 bytes) per cycle: a 16-byte read
 // instruction is serviced 16 lanes at a time and an 8-byte one 32 lanes at a
 // time, so the layouts below spread those lane groups over 16 distinct
 // 16-byte bank units.
 //
-// K-major operand stage (rows = M or N index, kDCpr chunks of 16 bytes of K
+// K-major operand slot (rows = M or N index, kDCpr chunks of 16 bytes of K
 // per row): the kDRpb rows r of one 256-byte bank row B = r / kDRpb hold
 // chunk c at unit ((r % kDRpb) * kDCpr + c) ^ (B % kDCpr), so 16 consecutive
-// rows reading the same chunk hit 16 different units.  Each load instruction
-// covers whole 128-byte row pieces when kDKBytes = 128.
+// rows reading the same chunk hit 16 different units.
 //
-// MN-major operand stage (rows = K index, 256 MN values = 512 bytes per row):
+// MN-major operand slot (rows = K index, 256 MN values = 512 bytes per row):
 // 16-byte unit u of row k sits at unit u ^ (4 (k & 3)).  A fragment is read
 // with two ds_read_b64_tr_b16: in each 16-lane group, lane p fetches 4
 // consecutive MN values of K row k0 + (p >> 2); the hardware hands lane p the
 // 4 K values of MN column (p) -- the same lane -> (row, K) assignment as a
 // K-major 16-byte fragment read.
-constexpr int kDKBytes = 64;                    // K bytes per row per stage (32 bf16)
-constexpr int kDStages = 4;
+constexpr int kDKBytes = 128;                   // K bytes per row per step (64 bf16)
+constexpr int kDSlots = 5;
 constexpr int kDSub = kDKBytes / 32;            // 16-wide MFMA sub-steps per K step
 constexpr int kDCpr = kDKBytes / 16;            // chunks per K-major row
 constexpr int kDRpb = 256 / kDKBytes;           // K-major rows per 256-byte bank row
-constexpr int kDLoads = kDKBytes / 16;          // load instructions per wave per operand per stage
-constexpr int kDOperand = kTile * kDKBytes;
-constexpr int kDStage = 2 * kDOperand;
-constexpr int kDLdsBytes = kDStages * kDStage;
-// loads in flight per wave behind the stage being waited for
-constexpr int kDWaitLoads = (kDStages - 2) * 2 * kDLoads;
+constexpr int kDLoads = kDKBytes / 16;          // load instructions per wave per operand per step
+constexpr int kDOperand = kTile * kDKBytes;     // one slot
+constexpr int kDLdsBytes = kDSlots * kDOperand;
 static_assert(kDLdsBytes <= 160 * 1024, "LDS capacity");
-static_assert((kDStages & (kDStages - 1)) == 0, "ring slots use a power-of-two mask");
+static_assert(kDSub == 4 && kDLoads == 8, "the K loop issues two loads per MFMA group");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define FLCE_AS3 __attribute__((address_space(3)))
@@ -570,28 +574,10 @@ struct MNMajorDirect {
 // after which other waves refill the stage this wave has just read.
 #define FLCE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
 
-template <class LA, class LB>
-__device__ __forceinline__ void issue_loads(LA& la, LB& lb, char* stage, int idx) {
-  if (idx < kDLoads)
-    la.issue_part(stage, idx);
-  else
-    lb.issue_part(stage + kDOperand, idx - kDLoads);
-}
-
-// K loop of the direct-to-LDS pipeline.  Per K step, kDSub sub-steps of 16
-// MFMAs per wave, each split into 4 block-row groups fenced in program order;
-// alongside each group the next sub-step's fragments are read (B first).  The
-// 2 * kDLoads loads for kDStages - 1 steps ahead are spread over the groups of
-// the first half of the step.  Before the last sub-step the wave waits for the
-// next stage's loads and its own LDS reads, and the barrier both publishes
-// that stage and frees the one just read; the last sub-step then runs while
-// sub-step 0 of the next stage is read.  The products are added to the
-// values `acc` holds on entry; kLoadedAcc says that those were loaded from
-// memory just before the call.
 // Marks every accumulator as used here.  When the accumulators were loaded
 // from memory, the compiler's own wait for those loads lands on this point
-// (where it costs one wait per tile) instead of on the first MFMA inside the
-// K loop, where it would drain the load pipeline every step.
+// (one wait per tile) instead of on the first MFMA inside the K loop, where
+// it would drain the load pipeline every step.
 __device__ __forceinline__ void touch_acc(f32x16 (&acc)[4][4]) {
   asm volatile(""
                : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
@@ -600,63 +586,81 @@ __device__ __forceinline__ void touch_acc(f32x16 (&acc)[4][4]) {
                  "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 }
 
+// K loop of the direct-to-LDS pipeline.  Per K step, four sub-steps of 16
+// MFMAs per wave, each split into 4 block-row groups fenced in program order;
+// alongside each group the next sub-step's fragments are read (B first).
+// Sub-step 0 issues A_{t+2} (two loads per group).  Before the last sub-step
+// the wave waits for A_{t+1} and B_{t+1} and for its own LDS reads, and the
+// barrier both publishes them and frees the slots of A_t and B_t; the last
+// sub-step then runs from registers while reading sub-step 0 of step t + 1
+// and issuing B_{t+2}.  The products are added to the values `acc` holds on
+// entry; kLoadedAcc says that those were loaded from memory just before the
+// call.  Ends with every load landed and a barrier, after which the LDS may
+// be reused by the epilogue.
 template <bool kLoadedAcc = false, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   if (nk <= 0) return;
+  auto slot = [&](int q) -> char* { return smem + q * kDOperand; };
+  auto issue_all = [&](auto& ld, int q) {
 #pragma unroll
-  for (int s = 0; s < kDStages - 1; ++s) {
-#pragma unroll
-    for (int i = 0; i < 2 * kDLoads; ++i) issue_loads(la, lb, smem + s * kDStage, i);
-    la.advance();
-    lb.advance();
-  }
-  FLCE_WAIT_VMCNT(kDWaitLoads);
+    for (int j = 0; j < kDLoads; ++j) ld.issue_part(slot(q), j);
+    ld.advance();
+  };
+  issue_all(la, 0);
+  issue_all(lb, 1);
+  issue_all(la, 2);
+  issue_all(lb, 3);
+  FLCE_WAIT_VMCNT(2 * kDLoads);
   __syncthreads();
   if constexpr (kLoadedAcc) touch_acc(acc);
-  constexpr int kLoadGroups = kDSub / 2 * 4;             // groups that issue loads
-  constexpr int kPerGroup = 2 * kDLoads / kLoadGroups;   // loads per such group
-  static_assert(kPerGroup * kLoadGroups == 2 * kDLoads, "even load spread");
   u32x4 a[2][4], b[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    b[0][i] = lb.read(smem + kDOperand, i, 0);
-    a[0][i] = la.read(smem, i, 0);
+    b[0][i] = lb.read(slot(1), i, 0);
+    a[0][i] = la.read(slot(0), i, 0);
   }
+  int sa = 0, sb = 1, sfree = 4;   // slots of A_t, B_t and of B_{t-1} (free)
   for (int it = 0; it < nk; ++it) {
-    const char* cur = smem + (it & (kDStages - 1)) * kDStage;
-    const char* nxt = smem + ((it + 1) & (kDStages - 1)) * kDStage;
-    char* dst = smem + ((it + kDStages - 1) & (kDStages - 1)) * kDStage;
+    const int na = sa + 2 >= kDSlots ? sa + 2 - kDSlots : sa + 2;
+    const int nb = sb + 2 >= kDSlots ? sb + 2 - kDSlots : sb + 2;
 #pragma unroll
     for (int ks = 0; ks < kDSub; ++ks) {
       const int p = ks & 1, q = p ^ 1;
       const bool last = ks == kDSub - 1;
       if (last) {
-        la.advance();
-        lb.advance();
         FLCE_FENCE();
-        FLCE_WAIT_VMCNT_LDS(kDWaitLoads);
+        FLCE_WAIT_VMCNT_LDS(kDLoads);
         __syncthreads();
         FLCE_FENCE();
       }
-      const char* src = last ? nxt : cur;
+      const char* srca = slot(last ? na : sa);
+      const char* srcb = slot(last ? nb : sb);
       const int nks = last ? 0 : ks + 1;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         FLCE_FENCE();
         mma_row(acc, a[p][g], b[p], g, bf16{});
         if (g < 2) {
-          b[q][2 * g] = lb.read(src + kDOperand, 2 * g, nks);
-          b[q][2 * g + 1] = lb.read(src + kDOperand, 2 * g + 1, nks);
+          b[q][2 * g] = lb.read(srcb, 2 * g, nks);
+          b[q][2 * g + 1] = lb.read(srcb, 2 * g + 1, nks);
         } else {
-          a[q][2 * g - 4] = la.read(src, 2 * g - 4, nks);
-          a[q][2 * g - 3] = la.read(src, 2 * g - 3, nks);
+          a[q][2 * g - 4] = la.read(srca, 2 * g - 4, nks);
+          a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
         }
-        if (ks < kDSub / 2) {
-#pragma unroll
-          for (int i = 0; i < kPerGroup; ++i) issue_loads(la, lb, dst, (ks * 4 + g) * kPerGroup + i);
+        if (ks == 0) {
+          la.issue_part(slot(sfree), 2 * g);
+          la.issue_part(slot(sfree), 2 * g + 1);
+        } else if (last) {
+          lb.issue_part(slot(sa), 2 * g);
+          lb.issue_part(slot(sa), 2 * g + 1);
         }
       }
+      if (ks == 0) la.advance();
     }
+    lb.advance();
+    sfree = sb;
+    sa = na;
+    sb = nb;
   }
   FLCE_FENCE();
   FLCE_WAIT_VMCNT(0);
