@@ -88,8 +88,9 @@ def summarize_traffic(kernel: str, fetch_dir: str, write_dir: str, copy_fetch_di
     """Turn four rocprofv3 --pmc runs into HBM bytes per launch of `kernel`."""
     cf = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copy")
     cw = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", "copy")
-    kf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", kernel)
-    kw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", kernel)
+    # "grad_h" must not also match grad_h_reduce_kernel
+    kf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", kernel + "_kernel")
+    kw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", kernel + "_kernel")
     if not (cf and cw and kf and kw):
         log("[bench] missing counter values")
         return 1
