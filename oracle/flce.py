@@ -27,7 +27,14 @@ pages rely on.  Readings where the pages are silent:
 * the argmax is taken over the capped logits and the lowest index wins ties;
 * ``grad_h`` is the gradient with respect to the caller's (un-multiplied) h
   and ``grad_W`` the gradient of this call alone (not accumulated across
-  calls); the upstream gradient of the scalar loss is 1.
+  calls); the upstream gradient of the scalar loss is ``grad_scale``
+  (default 1);
+* reduction "none" keeps the per-row losses (``loss_rows``; the scalar
+  ``loss`` is then their sum) and takes the upstream gradient of row i's loss
+  from ``grad_rows[i]`` (default 1 for every row), as torch's
+  ``cross_entropy(..., reduction="none")`` backward does.  The per-row
+  outputs answer the predicted-tokens contract of the Muse Glimmer page
+  (Testing Done) and the DeepSeek-V3 page (Summary).
 
 Every array is float64.  bf16 and fp32 inputs widen to float64 exactly.
 """
@@ -41,12 +48,24 @@ def _f64(x) -> np.ndarray:
 
 
 def reduction_scale(n_valid: int, reduction: str) -> float:
-    """s: 1/N_valid for "mean" (0 when nothing is valid), 1 for "sum"."""
+    """s: 1/N_valid for "mean" (0 when nothing is valid), 1 for "sum" and
+    "none"."""
     if reduction == "mean":
         return 1.0 / n_valid if n_valid > 0 else 0.0
-    if reduction == "sum":
+    if reduction in ("sum", "none"):
         return 1.0
     raise ValueError(f"unknown reduction {reduction!r}")
+
+
+def row_weights(N: int, n_valid: int, reduction: str, grad_rows=None, grad_scale: float = 1.0):
+    """Upstream gradient of each row's loss: s * grad_scale, times
+    grad_rows[i] with reduction "none"."""
+    w = np.full(N, reduction_scale(n_valid, reduction) * float(grad_scale))
+    if grad_rows is not None:
+        if reduction != "none":
+            raise ValueError("grad_rows needs reduction 'none'")
+        w = w * _f64(grad_rows).reshape(N)
+    return w
 
 
 def _valid_mask(labels: np.ndarray, V: int, ignore_index: int) -> np.ndarray:
@@ -90,13 +109,14 @@ def _dlogits(z, a, lse, labels, valid, s, softcap_T):
     """d loss / d a for a block of rows.
 
     d loss / d z = s * (softmax(z) - onehot(label)) on valid rows, 0 on ignored
-    rows; chained through the softcap, dz/da = 1 - tanh^2(a / T).
+    rows; chained through the softcap, dz/da = 1 - tanh^2(a / T).  ``s`` is a
+    scalar or one weight per row.
     """
     p = np.exp(z - lse[:, None])
     dz = p
     rows = np.nonzero(valid)[0]
     dz[rows, labels[rows]] -= 1.0
-    dz *= s
+    dz *= np.asarray(s)[:, None] if np.ndim(s) == 1 else s
     dz[~valid] = 0.0
     if softcap_T > 0:
         dz *= 1.0 - np.tanh(a / softcap_T) ** 2
@@ -104,7 +124,8 @@ def _dlogits(z, a, lse, labels, valid, s, softcap_T):
 
 
 def flce_reference(h, W, labels, ignore_index: int = -100, softcap_T: float = 0.0,
-                   multiplier: float = 1.0, reduction: str = "mean") -> dict:
+                   multiplier: float = 1.0, reduction: str = "mean", grad_rows=None,
+                   grad_scale: float = 1.0) -> dict:
     """Full forward and backward of FLCE for shapes that fit as one [N, V]
     array.  Returns loss, grad_h, grad_W, n_correct and per-row quantities."""
     h = _f64(h)
@@ -114,6 +135,7 @@ def flce_reference(h, W, labels, ignore_index: int = -100, softcap_T: float = 0.
     valid = _valid_mask(labels, V, ignore_index)
     n_valid = int(valid.sum())
     s = reduction_scale(n_valid, reduction)
+    w = row_weights(N, n_valid, reduction, grad_rows, grad_scale)
     a, z = capped_logits(h, W, multiplier, softcap_T)
     M, lse, pred, margin = _row_quantities(z)
     safe = np.where(valid, labels, 0)
@@ -121,7 +143,7 @@ def flce_reference(h, W, labels, ignore_index: int = -100, softcap_T: float = 0.
     loss_rows = np.where(valid, lse - z_label, 0.0)
     loss = s * loss_rows.sum()
     correct = valid & (pred == labels)
-    da = _dlogits(z, a, lse, safe, valid, s, softcap_T)
+    da = _dlogits(z, a, lse, safe, valid, w, softcap_T)
     grad_h = float(multiplier) * (da @ W)
     grad_W = float(multiplier) * (da.T @ h)
     return dict(loss=loss, grad_h=grad_h, grad_W=grad_W, n_correct=int(correct.sum()),

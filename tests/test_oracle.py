@@ -15,7 +15,10 @@ side of the cap, the wrong mean denominator) fails at least one of them:
 * central finite differences on tiny shapes with a strongly nonlinear cap;
 * torch's fp64 cross_entropy + autograd on the explicitly capped logits (an
   independent library implementation of the same composite);
-* brute-force argmax with ties.
+* brute-force argmax with ties;
+* per-row upstream gradients (reduction "none") and a scalar upstream
+  gradient against torch's fp64 autograd with those upstream gradients, plus
+  linearity in the row weights.
 """
 import math
 
@@ -227,6 +230,60 @@ def test_torch_fp64_cross_entropy_and_autograd(T, m, reduction):
     pred = torch.argmax(logits, dim=1).numpy()
     valid = labels != IGN
     assert r["n_correct"] == int(np.sum(valid & (pred == labels)))
+
+
+@pytest.mark.parametrize("T,m", [(0.0, 1.0), (1.5, 0.6)])
+def test_torch_fp64_reduction_none_with_row_gradients(T, m):
+    torch = pytest.importorskip("torch")
+    h, W, labels = _rand(14, 6, 29, seed=21, scale=0.8, n_ign=3)
+    w = np.random.default_rng(5).normal(size=14)          # any sign
+    r = flce_reference(h, W, labels, IGN, T, m, "none", grad_rows=w)
+    th = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    logits = torch.nn.functional.linear(th, tW) * m
+    if T > 0:
+        logits = T * torch.tanh(logits / T)
+    rows = torch.nn.functional.cross_entropy(logits, torch.tensor(labels), ignore_index=IGN,
+                                             reduction="none")
+    rows.backward(torch.tensor(w))
+    np.testing.assert_allclose(r["loss_rows"], rows.detach().numpy(), rtol=1e-13, atol=1e-15)
+    assert r["loss"] == pytest.approx(rows.detach().sum().item(), rel=1e-13)
+    np.testing.assert_allclose(r["grad_h"], th.grad.numpy(), rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(r["grad_W"], tW.grad.numpy(), rtol=1e-11, atol=1e-15)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_torch_fp64_upstream_scalar_gradient(reduction):
+    torch = pytest.importorskip("torch")
+    h, W, labels = _rand(12, 5, 17, seed=22, scale=0.9, n_ign=2)
+    g = -0.37
+    r = flce_reference(h, W, labels, IGN, 2.0, 0.8, reduction, grad_scale=g)
+    th = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    logits = 2.0 * torch.tanh(torch.nn.functional.linear(th, tW) * 0.8 / 2.0)
+    loss = torch.nn.functional.cross_entropy(logits, torch.tensor(labels), ignore_index=IGN,
+                                             reduction=reduction)
+    loss.backward(torch.tensor(g, dtype=torch.float64))
+    np.testing.assert_allclose(r["grad_h"], th.grad.numpy(), rtol=1e-11, atol=1e-15)
+    np.testing.assert_allclose(r["grad_W"], tW.grad.numpy(), rtol=1e-11, atol=1e-15)
+
+
+def test_row_gradients_are_linear_and_reduce_to_sum():
+    h, W, labels = _rand(10, 4, 13, seed=23, scale=0.6, n_ign=2)
+    rng = np.random.default_rng(6)
+    w1, w2 = rng.normal(size=10), rng.normal(size=10)
+    r1 = flce_reference(h, W, labels, IGN, 1.0, 1.0, "none", grad_rows=w1)
+    r2 = flce_reference(h, W, labels, IGN, 1.0, 1.0, "none", grad_rows=w2)
+    r12 = flce_reference(h, W, labels, IGN, 1.0, 1.0, "none", grad_rows=w1 - 3.0 * w2)
+    for k in ("grad_h", "grad_W"):
+        np.testing.assert_allclose(r12[k], r1[k] - 3.0 * r2[k], rtol=1e-10, atol=1e-13)
+    rs = flce_reference(h, W, labels, IGN, 1.0, 1.0, "sum")
+    rn = flce_reference(h, W, labels, IGN, 1.0, 1.0, "none")
+    assert rn["loss"] == pytest.approx(rs["loss"], rel=1e-14)
+    for k in ("grad_h", "grad_W"):
+        np.testing.assert_allclose(rn[k], rs[k], rtol=1e-14, atol=1e-16)
+    with pytest.raises(ValueError):
+        flce_reference(h, W, labels, IGN, 1.0, 1.0, "mean", grad_rows=w1)
 
 
 # --------------------------------------------------------------------- argmax
