@@ -23,12 +23,15 @@
  *   G_iv  = s * (softmax(z_i)_v - [v = label_i]) * (1 - (z_iv / T)^2)  on valid rows, 0 otherwise
  *   grad_h = m * G W        [N, H], dtype of h
  *   grad_W = m * G^T h      [V, H], fp32 (overwritten, not accumulated)
- * A row is valid when label_i != ignore_index.  The upstream gradient of the
- * scalar loss is taken as 1; callers scale the outputs themselves.
+ * A row is valid when label_i != ignore_index.  flce_fwd_bwd takes the
+ * upstream gradient of the scalar loss as 1; flce_fwd_bwd_ex adds an upstream
+ * gradient, per-row outputs, per-row losses without reduction and
+ * accumulation into grad_W (flce_options_t), and flce_fwd computes the loss
+ * alone.
  *
  * The library allocates no device memory and never synchronises inside
- * flce_fwd_bwd: all work is enqueued on the caller's stream and the caller
- * owns every buffer, including the workspace.
+ * flce_fwd_bwd, flce_fwd_bwd_ex or flce_fwd: all work is enqueued on the
+ * caller's stream and the caller owns every buffer, including the workspace.
  */
 #ifndef FLCE_H_
 #define FLCE_H_
@@ -45,8 +48,13 @@ extern "C" {
 /* Storage dtype of h, W and grad_h. */
 typedef enum { FLCE_DTYPE_BF16 = 0, FLCE_DTYPE_F32 = 1 } flce_dtype;
 
-/* Reduction of the per-row losses. */
-typedef enum { FLCE_REDUCTION_MEAN = 0, FLCE_REDUCTION_SUM = 1 } flce_reduction;
+/*
+ * Reduction of the per-row losses.  FLCE_REDUCTION_NONE (flce_fwd_bwd_ex and
+ * flce_fwd only) keeps the per-row losses (options.loss_rows, required): the
+ * scalar `loss` then receives their sum and row i's gradient is scaled by the
+ * upstream gradient options.grad_rows[i] (1 when grad_rows is NULL).
+ */
+typedef enum { FLCE_REDUCTION_MEAN = 0, FLCE_REDUCTION_SUM = 1, FLCE_REDUCTION_NONE = 2 } flce_reduction;
 
 /* Return codes. */
 enum {
@@ -104,7 +112,7 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t bu
  *              n_correct and from the gradients.
  *   softcap_T  logit softcap T; T <= 0 disables the cap.
  *   multiplier output multiplier m, applied to the logits before the cap.
- *   reduction  FLCE_REDUCTION_MEAN or FLCE_REDUCTION_SUM.
+ *   reduction  FLCE_REDUCTION_MEAN or FLCE_REDUCTION_SUM (NONE: flce_fwd_bwd_ex).
  *   loss       [1] fp32, written.
  *   grad_h     [N, H] dtype, written (gradient w.r.t. the caller's h); 16-byte aligned.
  *   grad_W     [V, H] fp32, overwritten with this call's gradient; 16-byte aligned.
@@ -135,8 +143,71 @@ int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels,
                  hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes);
 
 /*
+ * Options of flce_fwd_bwd_ex and flce_fwd.  The per-row outputs and the
+ * upstream gradient complete the output contract of the Liger-Kernel pages
+ * (Muse Glimmer page, Testing Done: the token_accuracy / predicted_tokens
+ * contract; DeepSeek-V3 page, Summary: token_accuracy / predicted_tokens
+ * returned); accumulation into grad_W serves gradient accumulation over
+ * micro-batches (SpecForge page, Changes: accumulation prepass).
+ * Zero-initialise the struct and set what is needed: every NULL output is
+ * skipped, grad_scale = 0 is read as 1.  All pointers are device pointers.
+ */
+typedef struct {
+  float* loss_rows;        /* [N] fp32 out: lse_i - z_{i,label_i} on valid rows, 0 on ignored
+                              rows; 4-byte aligned; required with FLCE_REDUCTION_NONE */
+  float* lse_rows;         /* [N] fp32 out: log-sum-exp of every row's capped logits */
+  int64_t* pred_rows;      /* [N] int64 out: first argmax of every row's capped logits
+                              (the predicted token); 8-byte aligned */
+  const float* grad_rows;  /* [N] fp32 in: upstream gradient of each row's loss; only with
+                              FLCE_REDUCTION_NONE (NULL = 1 for every row) */
+  float grad_scale;        /* upstream gradient of the scalar loss: multiplies grad_h and
+                              this call's grad_W term (0 is read as 1); finite */
+  int accumulate_grad_W;   /* 0: grad_W = this call's gradient; 1: grad_W += it (grad_W must
+                              hold the running sum on entry) */
+} flce_options_t;
+
+/*
+ * flce_fwd_bwd with options (may be NULL: then identical to flce_fwd_bwd).
+ * Same arguments, workspace and errors as flce_fwd_bwd; `reduction` may also
+ * be FLCE_REDUCTION_NONE.  FLCE_EINVAL also for: REDUCTION_NONE without
+ * loss_rows, grad_rows with another reduction, a non-finite grad_scale or a
+ * misaligned row pointer.
+ */
+int flce_fwd_bwd_ex(const void* h, const void* W, const int64_t* labels,
+                    int64_t N, int64_t H, int64_t V,
+                    int64_t ignore_index, float softcap_T, float multiplier, int reduction,
+                    float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
+                    hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes,
+                    const flce_options_t* options);
+
+/*
+ * Workspace bytes needed by flce_fwd (forward only: no logits transient and
+ * no grad_h partials) under `budget_bytes` (0 = default).  0 if no plan fits
+ * or the shape is unsupported.
+ */
+size_t flce_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t budget_bytes);
+
+/*
+ * Forward only: loss, n_correct and the per-row outputs of `options`, with no
+ * gradient (the cross-entropy-only pass of the SpecForge page, Changes:
+ * compute only the backbone CE during the accumulation prepass).  No logits
+ * are stored at all, so tokens run in chunks as large as the workspace
+ * allows.  Arguments as flce_fwd_bwd without grad_h and grad_W; in `options`
+ * only loss_rows, lse_rows and pred_rows are used (grad_rows, grad_scale and
+ * accumulate_grad_W are ignored); `workspace` holds at least
+ * flce_fwd_workspace_size(N, H, V, dtype, 0) bytes.  The loss, lse and
+ * argmax of each row are bitwise the ones flce_fwd_bwd computes.
+ */
+int flce_fwd(const void* h, const void* W, const int64_t* labels,
+             int64_t N, int64_t H, int64_t V,
+             int64_t ignore_index, float softcap_T, float multiplier, int reduction,
+             float* loss, int64_t* n_correct,
+             hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes,
+             const flce_options_t* options);
+
+/*
  * Synchronise `stream` and return the device-side status of the last
- * flce_fwd_bwd that used `workspace`: FLCE_OK or FLCE_ELABEL.  Returns
+ * flce_fwd_bwd, flce_fwd_bwd_ex or flce_fwd that used `workspace`: FLCE_OK or FLCE_ELABEL.  Returns
  * FLCE_EINVAL for a null workspace and FLCE_EDEVICE if the copy fails.
  */
 int flce_read_status(const void* workspace, hipStream_t stream);
@@ -146,7 +217,7 @@ const char* flce_strerror(int code);
 
 /*
  * Measurement facility (not part of the method): per-kernel timing with HIP
- * events.  While enabled, every kernel that flce_fwd_bwd enqueues is
+ * events.  While enabled, every kernel that the entry points enqueue is
  * bracketed by two events recorded on the same stream, so the elapsed time is
  * that kernel's own duration on that stream.  Kinds index the arrays below.
  */
@@ -157,7 +228,7 @@ enum {
   FLCE_KERNEL_GRAD_LOGITS = 3,  /* softmax - onehot (x softcap derivative), in place */
   FLCE_KERNEL_GRAD_H = 4,       /* grad_h GEMM G W (vocabulary-split partials) */
   FLCE_KERNEL_GRAD_H_REDUCE = 5,/* sum of the partials, cast to the storage dtype */
-  FLCE_KERNEL_GRAD_W = 6,       /* grad_W GEMM G^T h, fp32 overwrite / read-modify-write */
+  FLCE_KERNEL_GRAD_W = 6,       /* grad_W GEMM G^T h, fp32 (overwrite, or on top of the stored grad_W) */
   FLCE_KERNEL_FINALIZE = 7,     /* loss scalar and n_correct */
   FLCE_KERNEL_ZERO = 8,         /* zero grad_W when N = 0 */
   FLCE_KERNEL_KINDS = 9

@@ -20,10 +20,15 @@ from ._lib import (  # noqa: F401
     FLCE_EWORKSPACE,
     FLCE_OK,
     FLCE_REDUCTION_MEAN,
+    FLCE_REDUCTION_NONE,
     FLCE_REDUCTION_SUM,
     KERNEL_KINDS,
     FlceError,
+    flce_fwd,
     flce_fwd_bwd,
+    flce_fwd_bwd_ex,
+    flce_fwd_workspace_size,
+    flce_options_t,
     flce_profile_enable,
     flce_profile_read,
     flce_plan,
@@ -31,4 +36,4 @@ from ._lib import (  # noqa: F401
     flce_strerror,
     flce_workspace_size,
 )
-from .torch_api import FlceOutputs, fwd_bwd, linear_cross_entropy  # noqa: F401
+from .torch_api import FlceForward, FlceOutputs, forward, fwd_bwd, linear_cross_entropy  # noqa: F401

@@ -17,6 +17,7 @@ FLCE_DTYPE_BF16 = 0
 FLCE_DTYPE_F32 = 1
 FLCE_REDUCTION_MEAN = 0
 FLCE_REDUCTION_SUM = 1
+FLCE_REDUCTION_NONE = 2
 
 FLCE_OK = 0
 FLCE_EINVAL = 1
@@ -26,8 +27,8 @@ FLCE_ELABEL = 4
 FLCE_EUNSUPPORTED = 5
 
 # Every symbol include/flce.h declares.
-EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_read_status", "flce_strerror",
-            "flce_profile_enable", "flce_profile_read")
+EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_fwd_bwd_ex", "flce_fwd_workspace_size",
+            "flce_fwd", "flce_read_status", "flce_strerror", "flce_profile_enable", "flce_profile_read")
 
 # Kernel kinds of the per-kernel timing facility (index order of the arrays).
 KERNEL_KINDS = ("label_scan", "fwd_logits", "row_merge", "grad_logits", "grad_h", "grad_h_reduce",
@@ -47,6 +48,18 @@ class flce_plan_t(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class flce_options_t(ctypes.Structure):
+    """Options of flce_fwd_bwd_ex / flce_fwd (device addresses as ints, 0 = none)."""
+    _fields_ = [
+        ("loss_rows", ctypes.c_void_p),
+        ("lse_rows", ctypes.c_void_p),
+        ("pred_rows", ctypes.c_void_p),
+        ("grad_rows", ctypes.c_void_p),
+        ("grad_scale", ctypes.c_float),
+        ("accumulate_grad_W", ctypes.c_int),
+    ]
 
 
 class FlceError(RuntimeError):
@@ -69,6 +82,14 @@ def _load() -> ctypes.CDLL:
     lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
                                  vp, vp, vp, vp, vp, i32, vp, sz]
     lib.flce_fwd_bwd.restype = i32
+    lib.flce_fwd_bwd_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
+                                    vp, vp, vp, vp, vp, i32, vp, sz, ctypes.POINTER(flce_options_t)]
+    lib.flce_fwd_bwd_ex.restype = i32
+    lib.flce_fwd_workspace_size.argtypes = [i64, i64, i64, i32, sz]
+    lib.flce_fwd_workspace_size.restype = sz
+    lib.flce_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
+                             vp, vp, vp, i32, vp, sz, ctypes.POINTER(flce_options_t)]
+    lib.flce_fwd.restype = i32
     lib.flce_read_status.argtypes = [vp, vp]
     lib.flce_read_status.restype = i32
     lib.flce_strerror.argtypes = [i32]
@@ -103,6 +124,32 @@ def flce_fwd_bwd(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_ind
     return int(_lib.flce_fwd_bwd(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier,
                                  reduction, loss, grad_h, grad_W, n_correct, stream, dtype,
                                  workspace, workspace_bytes))
+
+
+def _opts(options):
+    return None if options is None else ctypes.byref(options)
+
+
+def flce_fwd_bwd_ex(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_index: int,
+                    softcap_T: float, multiplier: float, reduction: int, loss: int, grad_h: int,
+                    grad_W: int, n_correct, stream: int, dtype: int, workspace: int,
+                    workspace_bytes: int, options) -> int:
+    """Raw call; ``options`` is a flce_options_t or None.  Returns the C return code."""
+    return int(_lib.flce_fwd_bwd_ex(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier,
+                                    reduction, loss, grad_h, grad_W, n_correct, stream, dtype,
+                                    workspace, workspace_bytes, _opts(options)))
+
+
+def flce_fwd_workspace_size(N: int, H: int, V: int, dtype: int, budget_bytes: int = 0) -> int:
+    return int(_lib.flce_fwd_workspace_size(N, H, V, dtype, budget_bytes))
+
+
+def flce_fwd(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_index: int,
+             softcap_T: float, multiplier: float, reduction: int, loss: int, n_correct, stream: int,
+             dtype: int, workspace: int, workspace_bytes: int, options) -> int:
+    """Raw forward-only call; returns the C return code."""
+    return int(_lib.flce_fwd(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
+                             loss, n_correct, stream, dtype, workspace, workspace_bytes, _opts(options)))
 
 
 def flce_read_status(workspace: int, stream: int) -> int:

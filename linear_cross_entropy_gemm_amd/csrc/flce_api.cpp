@@ -12,7 +12,7 @@ extern "C" int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budg
                          flce_plan_t* out) {
   if (!out) return FLCE_EINVAL;
   Plan p;
-  const int rc = flce::make_plan(N, H, V, dtype, budget_bytes, &p);
+  const int rc = flce::make_plan(N, H, V, dtype, budget_bytes, false, &p);
   if (rc != FLCE_OK) return rc;
   out->chunk_rows = p.C;
   out->n_chunks = p.n_chunks;
@@ -26,29 +26,56 @@ extern "C" int flce_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budg
 
 extern "C" size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t budget_bytes) {
   Plan p;
-  if (flce::make_plan(N, H, V, dtype, budget_bytes, &p) != FLCE_OK) return 0;
+  if (flce::make_plan(N, H, V, dtype, budget_bytes, false, &p) != FLCE_OK) return 0;
   return p.total;
 }
 
-extern "C" int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
-                            int64_t V, int64_t ignore_index, float softcap_T, float multiplier,
-                            int reduction, float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
-                            hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes) {
-  if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
-  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM) return FLCE_EINVAL;
-  if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
-  if (!W || !grad_W || !loss || !workspace) return FLCE_EINVAL;
-  if (N > 0 && (!h || !labels || !grad_h)) return FLCE_EINVAL;
-  if (std::isnan(softcap_T) || std::isinf(softcap_T) || !std::isfinite(multiplier)) return FLCE_EINVAL;
-  if (!aligned(W, 16) || !aligned(grad_W, 16) || !aligned(loss, 4) || !aligned(workspace, 256))
-    return FLCE_EINVAL;
-  if (N > 0 && (!aligned(h, 16) || !aligned(grad_h, 16) || !aligned(labels, 8))) return FLCE_EINVAL;
-  if (n_correct && !aligned(n_correct, 8)) return FLCE_EINVAL;
+extern "C" size_t flce_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t budget_bytes) {
   Plan p;
-  const int rc = flce::make_plan(N, H, V, dtype, workspace_bytes, &p);
-  if (rc != FLCE_OK) return rc;
-  if (p.total > workspace_bytes) return FLCE_EWORKSPACE;
+  if (flce::make_plan(N, H, V, dtype, budget_bytes, true, &p) != FLCE_OK) return 0;
+  return p.total;
+}
 
+namespace {
+
+// Host-side checks shared by the entry points; nothing is enqueued before
+// they pass.  grad_h / grad_W are checked only when `with_grads`.
+int validate(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+             float softcap_T, float multiplier, int reduction, const float* loss, const void* grad_h,
+             const float* grad_W, const int64_t* n_correct, int dtype, const void* workspace,
+             const flce_options_t* o, bool with_grads) {
+  if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM && reduction != FLCE_REDUCTION_NONE)
+    return FLCE_EINVAL;
+  if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
+  if (!W || !loss || !workspace) return FLCE_EINVAL;
+  if (N > 0 && (!h || !labels)) return FLCE_EINVAL;
+  if (std::isnan(softcap_T) || std::isinf(softcap_T) || !std::isfinite(multiplier)) return FLCE_EINVAL;
+  if (!aligned(W, 16) || !aligned(loss, 4) || !aligned(workspace, 256)) return FLCE_EINVAL;
+  if (N > 0 && (!aligned(h, 16) || !aligned(labels, 8))) return FLCE_EINVAL;
+  if (n_correct && !aligned(n_correct, 8)) return FLCE_EINVAL;
+  if (with_grads) {
+    if (!grad_W || !aligned(grad_W, 16)) return FLCE_EINVAL;
+    if (N > 0 && (!grad_h || !aligned(grad_h, 16))) return FLCE_EINVAL;
+  }
+  if (reduction == FLCE_REDUCTION_NONE && (!o || !o->loss_rows)) return FLCE_EINVAL;
+  if (o) {
+    if (o->loss_rows && !aligned(o->loss_rows, 4)) return FLCE_EINVAL;
+    if (o->lse_rows && !aligned(o->lse_rows, 4)) return FLCE_EINVAL;
+    if (o->pred_rows && !aligned(o->pred_rows, 8)) return FLCE_EINVAL;
+    if (with_grads) {
+      if (o->grad_rows && (reduction != FLCE_REDUCTION_NONE || !aligned(o->grad_rows, 4))) return FLCE_EINVAL;
+      if (!std::isfinite(o->grad_scale)) return FLCE_EINVAL;
+      if (o->accumulate_grad_W != 0 && o->accumulate_grad_W != 1) return FLCE_EINVAL;
+    }
+  }
+  return FLCE_OK;
+}
+
+flce::CallArgs make_args(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                         int64_t V, int64_t ignore_index, float softcap_T, float multiplier,
+                         int reduction, float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
+                         int dtype, void* workspace, const flce_options_t* o, bool fwd_only) {
   flce::CallArgs a;
   a.h = h;
   a.W = W;
@@ -66,6 +93,61 @@ extern "C" int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels,
   a.grad_W = grad_W;
   a.n_correct = n_correct;
   a.workspace = workspace;
+  a.fwd_only = fwd_only;
+  if (o) {
+    a.loss_rows = o->loss_rows;
+    a.lse_rows = o->lse_rows;
+    a.pred_rows = o->pred_rows;
+    if (!fwd_only) {
+      a.grad_rows = o->grad_rows;
+      a.grad_scale = o->grad_scale == 0.0f ? 1.0f : o->grad_scale;
+      a.accumulate_grad_W = o->accumulate_grad_W != 0;
+    }
+  }
+  return a;
+}
+
+}  // namespace
+
+extern "C" int flce_fwd_bwd_ex(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                               int64_t V, int64_t ignore_index, float softcap_T, float multiplier,
+                               int reduction, float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
+                               hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes,
+                               const flce_options_t* options) {
+  int rc = validate(h, W, labels, N, H, V, softcap_T, multiplier, reduction, loss, grad_h, grad_W,
+                    n_correct, dtype, workspace, options, true);
+  if (rc != FLCE_OK) return rc;
+  Plan p;
+  rc = flce::make_plan(N, H, V, dtype, workspace_bytes, false, &p);
+  if (rc != FLCE_OK) return rc;
+  if (p.total > workspace_bytes) return FLCE_EWORKSPACE;
+  const flce::CallArgs a = make_args(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
+                                     loss, grad_h, grad_W, n_correct, dtype, workspace, options, false);
+  return flce::run_call(a, p, stream);
+}
+
+extern "C" int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                            int64_t V, int64_t ignore_index, float softcap_T, float multiplier,
+                            int reduction, float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
+                            hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes) {
+  if (reduction == FLCE_REDUCTION_NONE) return FLCE_EINVAL;   // needs options.loss_rows
+  return flce_fwd_bwd_ex(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction, loss,
+                         grad_h, grad_W, n_correct, stream, dtype, workspace, workspace_bytes, nullptr);
+}
+
+extern "C" int flce_fwd(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                        int64_t V, int64_t ignore_index, float softcap_T, float multiplier, int reduction,
+                        float* loss, int64_t* n_correct, hipStream_t stream, int dtype, void* workspace,
+                        size_t workspace_bytes, const flce_options_t* options) {
+  int rc = validate(h, W, labels, N, H, V, softcap_T, multiplier, reduction, loss, nullptr, nullptr,
+                    n_correct, dtype, workspace, options, false);
+  if (rc != FLCE_OK) return rc;
+  Plan p;
+  rc = flce::make_plan(N, H, V, dtype, workspace_bytes, true, &p);
+  if (rc != FLCE_OK) return rc;
+  if (p.total > workspace_bytes) return FLCE_EWORKSPACE;
+  const flce::CallArgs a = make_args(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
+                                     loss, nullptr, nullptr, n_correct, dtype, workspace, options, true);
   return flce::run_call(a, p, stream);
 }
 

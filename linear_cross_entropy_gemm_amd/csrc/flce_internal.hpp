@@ -22,9 +22,11 @@ constexpr int64_t kVocabTile = 256;
 constexpr int64_t kRowTile = 256;
 
 // Chunk plan and workspace layout (byte offsets from the workspace base).
+// A forward-only plan has no logits transient and no grad_h partials.
 struct Plan {
   int64_t N, H, V, es;
   int64_t C, n_chunks, Vp, nvt, split_k;
+  bool fwd_only;
   size_t off_lse, off_zlab, off_loss_row, off_pred;
   size_t off_pmax, off_psum, off_parg;
   size_t off_z, off_ghpart;
@@ -32,7 +34,7 @@ struct Plan {
 };
 
 // Returns FLCE_OK and fills `out`, or an error code (no plan fits the budget).
-int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* out);
+int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, bool fwd_only, Plan* out);
 
 struct CallArgs {
   const void* h;
@@ -42,10 +44,18 @@ struct CallArgs {
   float softcap_T, multiplier;
   int reduction, dtype;
   float* loss;
-  void* grad_h;
-  float* grad_W;
+  void* grad_h;       // unused when forward only
+  float* grad_W;      // unused when forward only
   int64_t* n_correct;
   void* workspace;
+  // options (flce_options_t); defaults: no row outputs, scale 1, overwrite
+  float* loss_rows = nullptr;
+  float* lse_rows = nullptr;
+  int64_t* pred_rows = nullptr;
+  const float* grad_rows = nullptr;
+  float grad_scale = 1.0f;
+  bool accumulate_grad_W = false;
+  bool fwd_only = false;
 };
 
 // Enqueue the whole call on `stream`.  Returns FLCE_OK or FLCE_EDEVICE.

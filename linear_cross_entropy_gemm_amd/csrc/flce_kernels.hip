@@ -11,7 +11,10 @@
 //   grad_h         partial[s] = G W over a slice of the vocabulary (MFMA)
 //   grad_h_reduce  grad_h rows = sum of the slices, cast to the storage dtype
 //   grad_W         grad_W (+)= G^T h_c (MFMA), fp32, overwrite on the first chunk
-// and once per call: header_init, label_scan (before), finalize (after).
+//                  unless the caller accumulates
+// and once per call: header_init, label_scan (before), finalize (after).  The
+// forward-only entry runs fwd_logits (without storing z) and row_merge per
+// chunk, then finalize.
 #include "kernel_args.hpp"
 #include "gemm_tile.hpp"
 
@@ -23,7 +26,7 @@ namespace flce {
 // per 32 x 32 block and 16 of its vocabulary entries, so the row statistics
 // reduce in registers first, then across lanes l and l + 32, then across the
 // two waves that share the tokens.
-template <typename T, bool kCap>
+template <typename T, bool kCap, bool kStoreZ>
 __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn,
                                              char* smem) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -92,7 +95,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
       }
     }
     if (found) p.zlab[tok] = zl;
-    if (tok_ok) {
+    if (kStoreZ && tok_ok) {
       T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + (int64_t)tok * p.ldz);
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
@@ -144,7 +147,9 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
   }
 }
 
-template <typename T>
+// kStoreZ: keep the capped logits for the backward (false on the forward-only
+// path, which needs only the row statistics).
+template <typename T, bool kStoreZ>
 __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
@@ -165,9 +170,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
     gemm_mainloop<T>(la, lb, (int)((kbytes + kKBytes - 1) / kKBytes), smem, acc);
   }
   if (p.T > 0.0f)
-    fwd_epilogue<T, true>(acc, p, tm, tn, smem);
+    fwd_epilogue<T, true, kStoreZ>(acc, p, tm, tn, smem);
   else
-    fwd_epilogue<T, false>(acc, p, tm, tn, smem);
+    fwd_epilogue<T, false, kStoreZ>(acc, p, tm, tn, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,7 +222,8 @@ __global__ __launch_bounds__(256) void grad_logits_kernel(GradLogitArgs p) {
   const bool valid = lab != p.ignore_index;
   const unsigned long long nv = p.hdr->n_valid;
   const float s = (p.reduction == FLCE_REDUCTION_MEAN) ? (nv ? 1.0f / (float)nv : 0.0f) : 1.0f;
-  const float scale = s * p.mult;
+  const float w = p.grad_rows ? p.grad_rows[row] : 1.0f;
+  const float scale = s * p.mult * p.grad_scale * w;
   const float l = p.lse[row];
   typedef T vec_t __attribute__((ext_vector_type(E)));
   vec_t zv = *reinterpret_cast<const vec_t*>(zr);
@@ -404,7 +410,8 @@ __global__ __launch_bounds__(256) void label_scan_kernel(const int64_t* labels, 
   }
 }
 
-// loss = s * sum of the per-row losses (fp64, fixed order), n_correct.
+// loss = s * sum of the per-row losses (fp64, fixed order; s = 1 for sum and
+// none), n_correct, and the requested per-row outputs.
 __global__ __launch_bounds__(1024) void finalize_kernel(FinalizeArgs p) {
   __shared__ double ls[1024];
   __shared__ long long cs[1024];
@@ -416,6 +423,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(FinalizeArgs p) {
       a += (double)p.loss_row[i];
       c += (p.pred[i] == lab) ? 1 : 0;
     }
+    if (p.loss_rows) p.loss_rows[i] = p.loss_row[i];
+    if (p.lse_rows) p.lse_rows[i] = p.lse[i];
+    if (p.pred_rows) p.pred_rows[i] = p.pred[i];
   }
   ls[threadIdx.x] = a;
   cs[threadIdx.x] = c;
@@ -473,7 +483,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
       label_scan_kernel<<<g < 1024 ? g : 1024, 256, 0, st>>>(a.labels, a.N, a.V, a.ignore_index, hdr);
     }
   }
-  if (pl.n_chunks == 0) {
+  if (pl.n_chunks == 0 && !a.fwd_only && !a.accumulate_grad_W) {
     ProfileScope ps(FLCE_KERNEL_ZERO, st);
     const int64_t n = a.V * a.H;
     const unsigned g = grid_1d(n, 256);
@@ -493,13 +503,16 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     f.ldh = a.H * es; f.ldw = a.H * es;
     f.C_this = Ct; f.H = H; f.V = V; f.Vp = Vp;
     f.mult = a.multiplier; f.T = capT; f.invT = invT;
-    f.z = zbuf; f.ldz = (int64_t)Vp * es;
+    f.z = a.fwd_only ? nullptr : zbuf; f.ldz = (int64_t)Vp * es;
     f.pmax = pmax; f.psum = psum; f.parg = parg; f.ldp = C;
     f.zlab = zlab + c0;
     f.map = TileMap{tiles_voc, tiles_tok, 1, 1, 0, 0};
     {
       ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
-      fwd_logits_kernel<T><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(f);
+      if (a.fwd_only)
+        fwd_logits_kernel<T, false><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(f);
+      else
+        fwd_logits_kernel<T, true><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(f);
     }
 
     MergeArgs m;
@@ -511,11 +524,13 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
       ProfileScope ps(FLCE_KERNEL_ROW_MERGE, st);
       row_merge_kernel<<<grid_1d(Ct, 64), 1024, 0, st>>>(m);
     }
+    if (a.fwd_only) continue;
 
     GradLogitArgs gl;
     gl.z = zbuf; gl.ldz = (int64_t)Vp * es; gl.C_this = Ct; gl.V = V; gl.Vp = Vp;
     gl.labels = lc; gl.ignore_index = a.ignore_index; gl.lse = lse + c0; gl.hdr = hdr;
     gl.reduction = a.reduction; gl.mult = a.multiplier; gl.T = capT; gl.invT = invT;
+    gl.grad_scale = a.grad_scale; gl.grad_rows = a.grad_rows ? a.grad_rows + c0 : nullptr;
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_LOGITS, st);
       grad_logits_kernel<T><<<grid_1d((int64_t)Ct * (Vp / Elem<T>::per_chunk), 256), 256, 0, st>>>(gl);
@@ -546,7 +561,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     GradWArgs gw;
     gw.G = zbuf; gw.ldg = (int64_t)Vp * es; gw.h = hc; gw.ldh = a.H * es;
     gw.C_this = Ct; gw.H = H; gw.V = V; gw.Vp = Vp;
-    gw.gW = a.grad_W; gw.accumulate = ck > 0 ? 1 : 0;
+    gw.gW = a.grad_W; gw.accumulate = (ck > 0 || a.accumulate_grad_W) ? 1 : 0;
     gw.map = TileMap{tiles_hid, tiles_voc, 1, 4, 1, 1};
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_W, st);
@@ -558,8 +573,9 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   }
   FinalizeArgs fa;
   fa.labels = a.labels; fa.N = a.N; fa.ignore_index = a.ignore_index;
-  fa.loss_row = loss_row; fa.pred = pred; fa.hdr = hdr; fa.reduction = a.reduction;
+  fa.loss_row = loss_row; fa.lse = lse; fa.pred = pred; fa.hdr = hdr; fa.reduction = a.reduction;
   fa.loss = a.loss; fa.n_correct = a.n_correct;
+  fa.loss_rows = a.loss_rows; fa.lse_rows = a.lse_rows; fa.pred_rows = a.pred_rows;
   {
     ProfileScope ps(FLCE_KERNEL_FINALIZE, st);
     finalize_kernel<<<1, 1024, 0, st>>>(fa);

@@ -7,6 +7,10 @@
 // runs at least two chunks and the full logits never exist.  With 288 GB of
 // HBM per MI355X the default 16 GiB budget never binds for the lm_head shapes
 // of the pages (Muse Glimmer 6656 x 202048, DeepSeek-V3 7168 x 129280).
+//
+// The forward-only plan stores no logits at all (only 12 bytes of partials
+// per token and 256-vocabulary tile), so its chunk is as large as the budget
+// allows, up to all N rows.
 #include <algorithm>
 
 #include "flce_internal.hpp"
@@ -61,14 +65,18 @@ void layout(Plan* p) {
   p->off_pmax = take(part);
   p->off_psum = take(part);
   p->off_parg = take(part);
-  p->off_z = take(size_t(p->C) * size_t(p->Vp) * size_t(p->es));
-  p->off_ghpart = take(size_t(p->split_k) * size_t(p->C) * size_t(p->H) * 4);
+  if (p->fwd_only) {
+    p->off_z = p->off_ghpart = 0;
+  } else {
+    p->off_z = take(size_t(p->C) * size_t(p->Vp) * size_t(p->es));
+    p->off_ghpart = take(size_t(p->split_k) * size_t(p->C) * size_t(p->H) * 4);
+  }
   p->total = off;
 }
 
 }  // namespace
 
-int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* out) {
+int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, bool fwd_only, Plan* out) {
   if (!out) return FLCE_EINVAL;
   if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
   if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
@@ -89,6 +97,7 @@ int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* o
   p.es = es;
   p.Vp = (V + kVocabTile - 1) / kVocabTile * kVocabTile;
   p.nvt = p.Vp / kVocabTile;
+  p.fwd_only = fwd_only;
   if (N == 0) {
     p.C = 0;
     p.n_chunks = 0;
@@ -98,8 +107,8 @@ int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, Plan* o
     *out = p;
     return FLCE_OK;
   }
-  const int64_t half = (N + 1) / 2;
-  int64_t c = half < kRowTile ? half : half / kRowTile * kRowTile;
+  const int64_t top = fwd_only ? N : (N + 1) / 2;
+  int64_t c = top < kRowTile ? top : top / kRowTile * kRowTile;
   for (;;) {
     p.C = c;
     p.n_chunks = (N + c - 1) / c;

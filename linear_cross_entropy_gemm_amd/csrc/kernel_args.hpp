@@ -48,6 +48,8 @@ struct GradLogitArgs {
   const Header* hdr;
   int reduction;
   float mult, T, invT;
+  float grad_scale;         // upstream gradient of the scalar loss
+  const float* grad_rows;   // per-row upstream gradients (reduction none) or null
 };
 
 struct GradHArgs {
@@ -85,11 +87,15 @@ struct FinalizeArgs {
   const int64_t* labels;
   int64_t N, ignore_index;
   const float* loss_row;
+  const float* lse;
   const int* pred;
   const Header* hdr;
   int reduction;
   float* loss;
   int64_t* n_correct;
+  float* loss_rows;     // optional per-row outputs (null: skipped)
+  float* lse_rows;
+  int64_t* pred_rows;
 };
 
 }  // namespace flce

@@ -1,5 +1,6 @@
 """PyTorch-facing wrappers: device memory and the current stream come from
-torch; the whole forward and backward runs in ``flce_fwd_bwd``."""
+torch; every step of the computation runs in ``flce_fwd_bwd_ex`` /
+``flce_fwd``."""
 from __future__ import annotations
 
 import dataclasses
@@ -10,44 +11,74 @@ import torch
 from . import _lib
 
 _DTYPES = {torch.bfloat16: _lib.FLCE_DTYPE_BF16, torch.float32: _lib.FLCE_DTYPE_F32}
-_REDUCTIONS = {"mean": _lib.FLCE_REDUCTION_MEAN, "sum": _lib.FLCE_REDUCTION_SUM}
+_REDUCTIONS = {"mean": _lib.FLCE_REDUCTION_MEAN, "sum": _lib.FLCE_REDUCTION_SUM,
+               "none": _lib.FLCE_REDUCTION_NONE}
 
 
 @dataclasses.dataclass
 class FlceOutputs:
-    loss: torch.Tensor        # [] fp32
+    loss: torch.Tensor        # [] fp32 (the sum of the row losses with reduction "none")
     grad_h: torch.Tensor      # [N, H] dtype of h
     grad_W: torch.Tensor      # [V, H] fp32
     n_correct: torch.Tensor   # [] int64
     workspace: torch.Tensor   # uint8, holds the status word
+    loss_rows: Optional[torch.Tensor] = None   # [N] fp32 (row outputs / reduction "none")
+    lse_rows: Optional[torch.Tensor] = None    # [N] fp32
+    pred_rows: Optional[torch.Tensor] = None   # [N] int64, predicted token of every row
+
+
+@dataclasses.dataclass
+class FlceForward:
+    loss: torch.Tensor
+    n_correct: torch.Tensor
+    workspace: torch.Tensor
+    loss_rows: Optional[torch.Tensor] = None
+    lse_rows: Optional[torch.Tensor] = None
+    pred_rows: Optional[torch.Tensor] = None
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
-            softcap: Optional[float] = None, multiplier: float = 1.0, reduction: str = "mean",
-            workspace: Optional[torch.Tensor] = None, out: Optional[FlceOutputs] = None,
-            check: bool = True) -> FlceOutputs:
-    """One call of ``flce_fwd_bwd`` on torch's current stream.
-
-    ``h`` [..., H] is flattened to [N, H] and ``grad_h`` restored to its shape
-    (SpecForge PR 1007, Changes: flatten rows for the vocabulary projection,
-    then restore the output shape)."""
+def _prepare(h, W, labels, reduction):
     if h.dtype not in _DTYPES or W.dtype != h.dtype:
         raise TypeError(f"h and W must both be bfloat16 or float32 (got {h.dtype}, {W.dtype})")
     if not h.is_cuda or not W.is_cuda or not labels.is_cuda:
         raise ValueError("h, W and labels must be on the GPU")
-    shape = h.shape
-    H = shape[-1]
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    H = h.shape[-1]
     h2 = h.reshape(-1, H).contiguous()
-    N = h2.shape[0]
-    V = W.shape[0]
-    Wc = W.contiguous()
     lab = labels.reshape(-1).to(torch.int64).contiguous()
-    if lab.numel() != N:
+    if lab.numel() != h2.shape[0]:
         raise ValueError("labels must have one entry per row of h")
+    return h2, W.contiguous(), lab
+
+
+def _row_buffers(N: int, dev, want: bool):
+    if not want:
+        return None, None, None
+    return (torch.empty(N, dtype=torch.float32, device=dev), torch.empty(N, dtype=torch.float32, device=dev),
+            torch.empty(N, dtype=torch.int64, device=dev))
+
+
+def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
+            softcap: Optional[float] = None, multiplier: float = 1.0, reduction: str = "mean",
+            workspace: Optional[torch.Tensor] = None, out: Optional[FlceOutputs] = None,
+            check: bool = True, *, grad_rows: Optional[torch.Tensor] = None, grad_scale: float = 1.0,
+            accumulate_grad_W: bool = False, row_outputs: bool = False) -> FlceOutputs:
+    """One call of ``flce_fwd_bwd_ex`` on torch's current stream.
+
+    ``h`` [..., H] is flattened to [N, H] and ``grad_h`` restored to its shape
+    (SpecForge PR 1007, Changes: flatten rows for the vocabulary projection,
+    then restore the output shape).  ``grad_rows`` (reduction "none") and
+    ``grad_scale`` are upstream gradients; with ``accumulate_grad_W`` the call
+    adds its weight gradient to ``out.grad_W``."""
+    h2, Wc, lab = _prepare(h, W, labels, reduction)
+    shape = h.shape
+    N, H = h2.shape
+    V = Wc.shape[0]
     dtype = _DTYPES[h.dtype]
     red = _REDUCTIONS[reduction]
     ws_bytes = _lib.flce_workspace_size(N, H, V, dtype, 0)
@@ -56,6 +87,8 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     dev = h.device
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if accumulate_grad_W and out is None:
+        raise ValueError("accumulate_grad_W needs out.grad_W holding the running sum")
     if out is None:
         out = FlceOutputs(
             loss=torch.empty((), dtype=torch.float32, device=dev),
@@ -64,32 +97,98 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
             n_correct=torch.empty((), dtype=torch.int64, device=dev),
             workspace=workspace,
         )
+    want_rows = row_outputs or reduction == "none"
+    if want_rows and out.loss_rows is None:
+        out.loss_rows, out.lse_rows, out.pred_rows = _row_buffers(N, dev, True)
+    gr = None
+    if grad_rows is not None:
+        gr = grad_rows.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
+        if gr.numel() != N:
+            raise ValueError("grad_rows must have one entry per row")
+    opts = _lib.flce_options_t(
+        loss_rows=_ptr(out.loss_rows) if want_rows else None,
+        lse_rows=_ptr(out.lse_rows) if want_rows else None,
+        pred_rows=_ptr(out.pred_rows) if want_rows else None,
+        grad_rows=_ptr(gr), grad_scale=float(grad_scale), accumulate_grad_W=1 if accumulate_grad_W else 0)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    rc = _lib.flce_fwd_bwd(_ptr(h2), _ptr(Wc), _ptr(lab), N, H, V, int(ignore_index),
-                           float(softcap) if softcap else 0.0, float(multiplier), red,
-                           _ptr(out.loss), _ptr(out.grad_h), _ptr(out.grad_W), _ptr(out.n_correct),
-                           stream, dtype, _ptr(workspace), int(workspace.numel()))
+    rc = _lib.flce_fwd_bwd_ex(_ptr(h2), _ptr(Wc), _ptr(lab), N, H, V, int(ignore_index),
+                              float(softcap) if softcap else 0.0, float(multiplier), red,
+                              _ptr(out.loss), _ptr(out.grad_h), _ptr(out.grad_W), _ptr(out.n_correct),
+                              stream, dtype, _ptr(workspace), int(workspace.numel()), opts)
     if rc != _lib.FLCE_OK:
-        raise _lib.FlceError(rc, "flce_fwd_bwd")
+        raise _lib.FlceError(rc, "flce_fwd_bwd_ex")
     if check:
         st = _lib.flce_read_status(_ptr(workspace), stream)
         if st != _lib.FLCE_OK:
-            raise _lib.FlceError(st, "flce_fwd_bwd (device status)")
+            raise _lib.FlceError(st, "flce_fwd_bwd_ex (device status)")
     out.grad_h = out.grad_h.reshape(shape)
     out.workspace = workspace
     return out
 
 
+def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
+            softcap: Optional[float] = None, multiplier: float = 1.0, reduction: str = "mean",
+            workspace: Optional[torch.Tensor] = None, check: bool = True,
+            row_outputs: bool = False) -> FlceForward:
+    """Loss and n_correct only (``flce_fwd``): the cross-entropy-only pass of
+    the SpecForge page (Changes), with no gradient and no stored logits."""
+    h2, Wc, lab = _prepare(h, W, labels, reduction)
+    N, H = h2.shape
+    V = Wc.shape[0]
+    dtype = _DTYPES[h.dtype]
+    ws_bytes = _lib.flce_fwd_workspace_size(N, H, V, dtype, 0)
+    if ws_bytes == 0:
+        raise _lib.FlceError(_lib.FLCE_EUNSUPPORTED, "flce_fwd_workspace_size")
+    dev = h.device
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    want_rows = row_outputs or reduction == "none"
+    loss_rows, lse_rows, pred_rows = _row_buffers(N, dev, want_rows)
+    res = FlceForward(loss=torch.empty((), dtype=torch.float32, device=dev),
+                      n_correct=torch.empty((), dtype=torch.int64, device=dev), workspace=workspace,
+                      loss_rows=loss_rows, lse_rows=lse_rows, pred_rows=pred_rows)
+    opts = _lib.flce_options_t(loss_rows=_ptr(loss_rows), lse_rows=_ptr(lse_rows), pred_rows=_ptr(pred_rows))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _lib.flce_fwd(_ptr(h2), _ptr(Wc), _ptr(lab), N, H, V, int(ignore_index),
+                       float(softcap) if softcap else 0.0, float(multiplier), _REDUCTIONS[reduction],
+                       _ptr(res.loss), _ptr(res.n_correct), stream, dtype, _ptr(workspace),
+                       int(workspace.numel()), opts)
+    if rc != _lib.FLCE_OK:
+        raise _lib.FlceError(rc, "flce_fwd")
+    if check:
+        st = _lib.flce_read_status(_ptr(workspace), stream)
+        if st != _lib.FLCE_OK:
+            raise _lib.FlceError(st, "flce_fwd (device status)")
+    return res
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
+    """mean / sum: the gradients come out of the fused forward call and are
+    scaled by the upstream scalar in backward.  none: the forward computes the
+    row losses only; backward recomputes the logits with the upstream row
+    gradients (grad_W mixes rows, so it cannot be rescaled afterwards)."""
+
     @staticmethod
     def forward(ctx, h, W, labels, ignore_index, softcap, multiplier, reduction):
+        ctx.w_dtype = W.dtype
+        ctx.reduction = reduction
+        if reduction == "none":
+            o = forward(h.detach(), W.detach(), labels, ignore_index, softcap, multiplier, "none")
+            ctx.save_for_backward(h.detach(), W.detach(), labels)
+            ctx.args = (ignore_index, softcap, multiplier)
+            return o.loss_rows.reshape(labels.shape), o.n_correct
         o = fwd_bwd(h.detach(), W.detach(), labels, ignore_index, softcap, multiplier, reduction)
         ctx.save_for_backward(o.grad_h, o.grad_W)
-        ctx.w_dtype = W.dtype
         return o.loss, o.n_correct
 
     @staticmethod
     def backward(ctx, grad_loss, _grad_n_correct):
+        if ctx.reduction == "none":
+            h, W, labels = ctx.saved_tensors
+            ignore_index, softcap, multiplier = ctx.args
+            o = fwd_bwd(h, W, labels, ignore_index, softcap, multiplier, "none",
+                        grad_rows=grad_loss.reshape(-1))
+            return o.grad_h, o.grad_W.to(ctx.w_dtype), None, None, None, None, None
         gh, gW = ctx.saved_tensors
         g = grad_loss.to(torch.float32)
         gh = gh * g.to(gh.dtype)
@@ -102,6 +201,5 @@ def linear_cross_entropy(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
                          multiplier: float = 1.0, reduction: str = "mean"):
     """Differentiable FLCE: returns (loss, n_correct); token accuracy is
     n_correct / number of non-ignored labels (Muse Glimmer page, Summary
-    item 2).  The gradients are computed in the forward call and scaled by
-    the upstream gradient in backward."""
+    item 2).  With reduction "none" the loss has the shape of ``labels``."""
     return _LinearCrossEntropy.apply(h, W, labels, ignore_index, softcap, multiplier, reduction)

@@ -118,7 +118,8 @@ def _call(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=3), L.FLCE_EINVAL),
-    (dict(reduction=2), L.FLCE_EINVAL),
+    (dict(reduction=2), L.FLCE_EINVAL),   # none needs flce_fwd_bwd_ex with loss_rows
+    (dict(reduction=3), L.FLCE_EINVAL),
     (dict(N=-1), L.FLCE_EINVAL),
     (dict(H=0), L.FLCE_EINVAL),
     (dict(V=0), L.FLCE_EINVAL),
@@ -144,6 +145,78 @@ def test_fwd_bwd_rejects_before_launch(kw, code):
     # the workspace check (64 bytes), so no variant can reach a launch; each
     # variant must be rejected by its own, earlier check.
     assert _call(**kw) == code
+
+
+def _opts(**kw):
+    o = L.flce_options_t()
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def _call_ex(opts, **kw):
+    args = dict(h=16, W=16, labels=8, N=4, H=8, V=8, ignore_index=-100, softcap_T=0.0,
+                multiplier=1.0, reduction=0, loss=4, grad_h=16, grad_W=16, n_correct=None,
+                stream=0, dtype=0, workspace=256, workspace_bytes=64)
+    args.update(kw)
+    return L.flce_fwd_bwd_ex(*args.values(), opts)
+
+
+@pytest.mark.parametrize("opts,kw,code", [
+    (None, dict(reduction=2), L.FLCE_EINVAL),                       # none without loss_rows
+    (_opts(lse_rows=64), dict(reduction=2), L.FLCE_EINVAL),
+    (_opts(loss_rows=64, grad_rows=64), dict(reduction=0), L.FLCE_EINVAL),   # row grads need none
+    (_opts(loss_rows=66), dict(reduction=2), L.FLCE_EINVAL),         # misaligned
+    (_opts(pred_rows=68), {}, L.FLCE_EINVAL),
+    (_opts(loss_rows=64, grad_rows=66), dict(reduction=2), L.FLCE_EINVAL),
+    (_opts(grad_scale=float("nan")), {}, L.FLCE_EINVAL),
+    (_opts(grad_scale=float("inf")), {}, L.FLCE_EINVAL),
+    (_opts(accumulate_grad_W=2), {}, L.FLCE_EINVAL),
+    (None, dict(grad_W=None), L.FLCE_EINVAL),
+    (None, {}, L.FLCE_EWORKSPACE),
+    (_opts(loss_rows=64, lse_rows=64, pred_rows=64, grad_rows=64, grad_scale=2.0, accumulate_grad_W=1),
+     dict(reduction=2), L.FLCE_EWORKSPACE),
+])
+def test_fwd_bwd_ex_rejects_before_launch(opts, kw, code):
+    # fake addresses and a 64-byte workspace: nothing can reach a launch
+    assert _call_ex(opts, **kw) == code
+
+
+def _call_fwd(opts, **kw):
+    args = dict(h=16, W=16, labels=8, N=4, H=8, V=8, ignore_index=-100, softcap_T=0.0,
+                multiplier=1.0, reduction=0, loss=4, n_correct=None, stream=0, dtype=0,
+                workspace=256, workspace_bytes=64)
+    args.update(kw)
+    return L.flce_fwd(*args.values(), opts)
+
+
+@pytest.mark.parametrize("opts,kw,code", [
+    (None, dict(reduction=2), L.FLCE_EINVAL),
+    (None, dict(W=None), L.FLCE_EINVAL),
+    (None, dict(loss=None), L.FLCE_EINVAL),
+    (None, dict(h=24), L.FLCE_EINVAL),
+    (_opts(lse_rows=66), {}, L.FLCE_EINVAL),
+    (None, dict(H=12), L.FLCE_EUNSUPPORTED),
+    (None, {}, L.FLCE_EWORKSPACE),
+    # gradient-only options are ignored by the forward-only entry
+    (_opts(loss_rows=64, grad_rows=66, grad_scale=float("nan"), accumulate_grad_W=7), dict(reduction=2),
+     L.FLCE_EWORKSPACE),
+])
+def test_fwd_rejects_before_launch(opts, kw, code):
+    assert _call_fwd(opts, **kw) == code
+
+
+def test_forward_only_plan_is_smaller_and_unchunked():
+    for N, H, V, dt in [(8192, 6656, 202048, 0), (32768, 7168, 129280, 0), (256, 128, 1024, 1), (1, 8, 8, 0)]:
+        fb = L.flce_workspace_size(N, H, V, dt)
+        fo = L.flce_fwd_workspace_size(N, H, V, dt)
+        assert 0 < fo < fb
+        # one chunk of all N rows: header + 4 row arrays + 3 partial arrays of [V/256, N]
+        nvt = (V + 255) // 256
+        assert fo >= 256 + 4 * 4 * N + 3 * 4 * nvt * N
+    # no logits transient: the c4 forward workspace stays under 0.1 GB
+    assert L.flce_fwd_workspace_size(8192, 6656, 202048, 0) < 1e8
+    assert L.flce_fwd_workspace_size(4, 12, 8, 0) == 0          # unsupported H
 
 
 def test_read_status_null():

@@ -11,7 +11,9 @@ Per workload (c2..c5 of ``synth.CONFIGS``):
   error <= 2e-2);
 * at every entry: grad_h of ignored rows is exactly zero; without a softcap
   every column of grad_W sums to zero up to the first-order effect of the
-  bf16 logit/gradient transients.
+  bf16 logit/gradient transients;
+* the forward-only entry point (c4, c5): loss, n_correct window and every
+  row's log-sum-exp against the stored oracle values.
 """
 import os
 
@@ -87,3 +89,30 @@ def test_full_size(name):
         f"grad_W rel {e_gW:.2e} ({len(vrows)} vocabulary rows)")
     assert e_gh <= 2e-2
     assert e_gW <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_full_size_forward_only(name):
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    cfg = synth.CONFIGS[name]
+    gold = np.load(os.path.join(GOLDEN, f"{name}_rowstats.npz"))
+    log(f"[full] forward only {name}: N={cfg.N} H={cfg.H} V={cfg.V}")
+    case = synth.make_case(cfg)
+    assert case.digest() == str(gold["digest"])
+    h, W, lab = to_device(case)
+    f = L.forward(h, W, lab, IGN, cfg.softcap_T if cfg.softcap_T > 0 else None, cfg.multiplier,
+                  cfg.reduction, row_outputs=True)
+    torch.cuda.synchronize()
+    ref_loss = float(gold["loss"])
+    e = abs(f.loss.item() - ref_loss) / abs(ref_loss)
+    lse = f.lse_rows.cpu().numpy().astype(np.float64)
+    e_lse = float(np.max(np.abs(lse - gold["lse"]) / np.maximum(np.abs(gold["lse"]), 1.0)))
+    valid = case.labels != IGN
+    lo, hi = oracle.n_correct_window(gold["pred"], gold["margin"], gold["z_label"], gold["M"],
+                                     case.labels, valid)
+    nc = int(f.n_correct.item())
+    log(f"[full] forward only {name}: loss rel {e:.2e}, max row lse rel {e_lse:.2e}, n_correct {nc} in [{lo}, {hi}]")
+    assert e <= 2e-3
+    assert e_lse <= 2e-3
+    assert lo <= nc <= hi
