@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "FLCE fwd+bwd tokens/sec at V=202048,H=6656 bf16; % of MFMA bf16 peak"
+METRIC_FWD = "FLCE forward-only tokens/sec at V=202048,H=6656 bf16; % of MFMA bf16 peak"
 # MI355X dense MFMA peaks (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 GEMM_KINDS = ("fwd_logits", "grad_h", "grad_W")
@@ -148,6 +149,45 @@ def cpu_baseline(case, n_tokens: int) -> dict:
                       f"(loss, argmax, grad_h rows, the sample's [V,H] grad_W) in {dt:.1f} s"}
 
 
+def cpu_baseline_forward(case, n_tokens: int) -> dict:
+    """The fp64 oracle's forward (row statistics over the full vocabulary) on
+    the first n_tokens rows of the same inputs."""
+    import oracle
+    import synth
+    cfg = case.cfg
+    n = min(n_tokens, cfg.N)
+    t0 = time.perf_counter()
+    oracle.row_stats(case.h_f32()[:n], case.W_f32(), case.labels[:n], synth.IGNORE_INDEX, cfg.softcap_T,
+                     cfg.multiplier)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {n} of {cfg.N} tokens of the same seeded inputs, fp64 forward "
+                      f"(log-sum-exp, label logit, argmax per row) in {dt:.1f} s"}
+
+
+def time_calls(call, stream, steps: int, warmup: int):
+    """warmup untimed calls, then `steps` timed ones between synchronizations,
+    with the library's per-kernel event timing on."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    L.flce_profile_enable(True)
+    L.flce_profile_read(stream.cuda_stream, reset=True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    prof = L.flce_profile_read(stream.cuda_stream, reset=True)
+    L.flce_profile_enable(False)
+    return ev0.elapsed_time(ev1) / steps, prof
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +202,9 @@ def main() -> int:
                     metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
                     help="write HBM traffic per launch from four rocprofv3 --pmc runs")
     ap.add_argument("--command", default="", help="command text recorded with --summarize-traffic")
+    ap.add_argument("--entry", default="fwd_bwd", choices=("fwd_bwd", "fwd"),
+                    help="fwd_bwd (default): flce_fwd_bwd, the headline metric; fwd: the forward-only "
+                         "flce_fwd (loss and n_correct, 2*N*H*V)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
@@ -198,38 +241,43 @@ def main() -> int:
     plan = L.flce_plan(cfg.N, cfg.H, cfg.V, dtype_code)
     log(f"[bench] plan {plan.as_dict()}")
 
-    o = L.fwd_bwd(h, W, lab, **kw)                      # allocates outputs + workspace, checks status
-    ws = o.workspace
-    for i in range(args.warmup):
-        L.fwd_bwd(h, W, lab, workspace=ws, out=o, check=False, **kw)
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps); loss {o.loss.item():.6f} n_correct {o.n_correct.item()}")
-
     stream = torch.cuda.current_stream(dev)
-    L.flce_profile_enable(True)
-    L.flce_profile_read(stream.cuda_stream, reset=True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        L.fwd_bwd(h, W, lab, workspace=ws, out=o, check=False, **kw)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    prof = L.flce_profile_read(stream.cuda_stream, reset=True)
-    L.flce_profile_enable(False)
+    fwd_only = args.entry == "fwd"
+    if fwd_only:
+        f = L.forward(h, W, lab, **kw)                  # allocates outputs + workspace, checks status
+        ws = f.workspace
+        red = {"mean": L.FLCE_REDUCTION_MEAN, "sum": L.FLCE_REDUCTION_SUM}[cfg.reduction]
+        raw = (h.data_ptr(), W.data_ptr(), lab.data_ptr(), cfg.N, cfg.H, cfg.V, synth.IGNORE_INDEX,
+               float(softcap or 0.0), float(cfg.multiplier), red, f.loss.data_ptr(), f.n_correct.data_ptr(),
+               stream.cuda_stream, dtype_code, ws.data_ptr(), ws.numel(), None)
+
+        def call():
+            rc = L.flce_fwd(*raw)
+            if rc != L.FLCE_OK:
+                raise L.FlceError(rc, "flce_fwd")
+        loss_t, nc_t = f.loss, f.n_correct
+    else:
+        o = L.fwd_bwd(h, W, lab, **kw)                  # allocates outputs + workspace, checks status
+        ws = o.workspace
+
+        def call():
+            L.fwd_bwd(h, W, lab, workspace=ws, out=o, check=False, **kw)
+        loss_t, nc_t = o.loss, o.n_correct
+    ms, prof = time_calls(call, stream, args.steps, args.warmup)
+    log(f"[bench] {args.entry}: loss {loss_t.item():.6f} n_correct {nc_t.item()}")
     st = L.flce_read_status(ws.data_ptr(), stream.cuda_stream)
     if st != L.FLCE_OK:
         raise L.FlceError(st, "device status after timing")
-    ms = ev0.elapsed_time(ev1) / args.steps
     tok_s = cfg.N / (ms * 1e-3)
-    flops = 6.0 * cfg.N * cfg.H * cfg.V
-    flops_valid = 6.0 * cfg.n_valid * cfg.H * cfg.V
+    n_gemm = 1 if fwd_only else 3
+    flops = 2.0 * n_gemm * cfg.N * cfg.H * cfg.V
+    flops_valid = 2.0 * n_gemm * cfg.n_valid * cfg.H * cfg.V
     peak = PEAK_TFLOPS[cfg.dtype]
     pct = flops / (ms * 1e-3) / (peak * 1e12) * 100.0
     pct_valid = flops_valid / (ms * 1e-3) / (peak * 1e12) * 100.0
+    basis = "2NHV" if fwd_only else "6NHV"
     log(f"[bench] {ms:.3f} ms/step, {tok_s:,.0f} tokens/s, {pct:.1f}% of MFMA peak "
-        f"(6NHV basis; {pct_valid:.1f}% on 6*N_valid*H*V)")
+        f"({basis} basis; {pct_valid:.1f}% on N_valid)")
 
     kernels = {}
     for k, (tot, n) in prof.items():
@@ -247,22 +295,25 @@ def main() -> int:
                 "flops_per_launch": flops_per_launch, "avg_launch_ms": round(kernels[dom]["avg_ms"], 4)}
 
     result = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC_FWD if fwd_only else METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "N": cfg.N, "H": cfg.H,
                    "V": cfg.V, "n_valid": cfg.n_valid, "softcap_T": cfg.softcap_T,
                    "multiplier": cfg.multiplier, "reduction": cfg.reduction,
-                   "chunk_rows": plan.chunk_rows, "n_chunks": plan.n_chunks, "split_k": plan.split_k,
+                   "entry": "flce_fwd" if fwd_only else "flce_fwd_bwd",
+                   "chunk_rows": cfg.N if fwd_only else plan.chunk_rows,
+                   "n_chunks": 1 if fwd_only else plan.n_chunks, "split_k": plan.split_k,
                    "parallelism": "single GPU"},
-        "pct_peak_6NHV": round(pct, 2), "pct_peak_6NvalidHV": round(pct_valid, 2),
+        f"pct_peak_{basis}": round(pct, 2), f"pct_peak_{basis.replace('N', 'Nvalid', 1)}": round(pct_valid, 2),
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on {args.cpu_tokens} tokens (host cores) ...")
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_tokens)
+        result["cpu_baseline"] = (cpu_baseline_forward(case, 3 * args.cpu_tokens) if fwd_only
+                                  else cpu_baseline(case, args.cpu_tokens))
         log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
     else:
         result["cpu_baseline"] = None
