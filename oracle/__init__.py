@@ -20,6 +20,7 @@ invariant on configs without a softcap.
 """
 from .flce import (  # noqa: F401
     capped_logits,
+    cross_entropy_on_logits,
     flce_reference,
     row_stats,
     grad_h_rows,

@@ -229,6 +229,32 @@ def grad_W_rows(h, W, labels, vocab_rows, lse, n_valid: int, ignore_index: int =
     return float(multiplier) * out
 
 
+def cross_entropy_on_logits(z, labels, ignore_index: int = -100, reduction: str = "mean",
+                            grad_rows=None, grad_scale: float = 1.0) -> dict:
+    """Cross-entropy of already materialised (and already capped) logits
+    z [N, V]: the non-fused branch the Liger-Kernel pages compare against
+    (Muse Glimmer page, Testing Done: the non-fused softcap branch;
+    DeepSeek-V3 page, Summary: with logits materialised the plain loss
+    function is used).  Returns the loss, per-row quantities and the gradient
+    with respect to z (softmax - onehot, scaled like the fused path; no
+    softcap derivative, since z is the input here)."""
+    z = _f64(z)
+    labels = np.asarray(labels, dtype=np.int64)
+    N, V = z.shape
+    valid = _valid_mask(labels, V, ignore_index)
+    n_valid = int(valid.sum())
+    s = reduction_scale(n_valid, reduction)
+    w = row_weights(N, n_valid, reduction, grad_rows, grad_scale)
+    M, lse, pred, margin = _row_quantities(z)
+    safe = np.where(valid, labels, 0)
+    z_label = z[np.arange(N), safe]
+    loss_rows = np.where(valid, lse - z_label, 0.0)
+    grad_z = _dlogits(z.copy(), z, lse, safe, valid, w, 0.0)
+    return dict(loss=s * loss_rows.sum(), loss_rows=loss_rows, lse=lse, pred=pred, M=M, margin=margin,
+                z_label=z_label, valid=valid, n_valid=n_valid,
+                n_correct=int(np.sum(valid & (pred == labels))), grad_z=grad_z)
+
+
 def n_correct_window(pred, margin, z_label, M, labels, valid, tol: float = 1e-2):
     """Range [lo, hi] that a correct n_correct must fall in.
 

@@ -286,6 +286,41 @@ def test_row_gradients_are_linear_and_reduce_to_sum():
         flce_reference(h, W, labels, IGN, 1.0, 1.0, "mean", grad_rows=w1)
 
 
+# ------------------------------------------- cross-entropy on given logits
+
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_cross_entropy_on_logits_is_flce_with_identity_weight(reduction):
+    # with W = I (H = V), m = 1 and no cap the logits are h itself, so the
+    # cross-entropy of given logits must equal the fused definition and its
+    # logit gradient must equal grad_h = dlogits @ I
+    rng = np.random.default_rng(31)
+    V = 23
+    z = 2.0 * rng.standard_normal((17, V))
+    labels = rng.integers(0, V, 17)
+    labels[[2, 9]] = IGN
+    ce = oracle.cross_entropy_on_logits(z, labels, IGN, reduction)
+    fl = flce_reference(z, np.eye(V), labels, IGN, 0.0, 1.0, reduction)
+    assert ce["loss"] == pytest.approx(fl["loss"], rel=1e-14)
+    np.testing.assert_allclose(ce["grad_z"], fl["grad_h"], rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(ce["lse"], fl["lse"], rtol=1e-15)
+    assert ce["n_correct"] == fl["n_correct"]
+
+
+def test_cross_entropy_on_logits_against_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(32)
+    z = 3.0 * rng.standard_normal((19, 41))
+    labels = rng.integers(0, 41, 19)
+    labels[[0, 5, 6]] = IGN
+    w = rng.normal(size=19)
+    ce = oracle.cross_entropy_on_logits(z, labels, IGN, "none", grad_rows=w)
+    tz = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+    rows = torch.nn.functional.cross_entropy(tz, torch.tensor(labels), ignore_index=IGN, reduction="none")
+    rows.backward(torch.tensor(w))
+    np.testing.assert_allclose(ce["loss_rows"], rows.detach().numpy(), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(ce["grad_z"], tz.grad.numpy(), rtol=1e-12, atol=1e-16)
+
+
 # --------------------------------------------------------------------- argmax
 
 def test_brute_force_argmax_with_ties():
