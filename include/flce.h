@@ -206,8 +206,48 @@ int flce_fwd(const void* h, const void* W, const int64_t* labels,
              const flce_options_t* options);
 
 /*
+ * Materialised-logits path: the non-fused branch the fused loss is compared
+ * against (Muse Glimmer page, Testing Done: the non-fused softcap branch, and
+ * skip_logits=False in evaluation; DeepSeek-V3 page, Summary: outside training
+ * with labels the logits are materialised and the plain loss runs on them).
+ *
+ * flce_logits writes z = T tanh(m h W^T / T) (T > 0) or m h W^T, [N, V], into
+ * `logits` (dtype of h; row stride `ld_logits` elements, ld_logits >= V and
+ * ld_logits * sizeof(dtype) a multiple of 16; 16-byte aligned).  Columns
+ * [V, ld_logits) are not written.  h, W, N, H, V, dtype as for flce_fwd_bwd.
+ * Returns FLCE_OK, FLCE_EINVAL, FLCE_EUNSUPPORTED or FLCE_EDEVICE; allocates
+ * nothing and needs no workspace.
+ */
+int flce_logits(const void* h, const void* W, int64_t N, int64_t H, int64_t V,
+                float softcap_T, float multiplier, void* logits, int64_t ld_logits,
+                hipStream_t stream, int dtype);
+
+/* Workspace bytes of flce_cross_entropy for N rows (256 + 3 * N * 4, padded). */
+size_t flce_cross_entropy_workspace_size(int64_t N);
+
+/*
+ * Cross-entropy of given logits z [N, V] (dtype; row stride ld_logits as for
+ * flce_logits; the logits are used as they are, so a softcap belongs in
+ * them): loss = s * sum_{valid i} (lse_i - z_{i,label_i}) with the reductions,
+ * options and per-row outputs of flce_fwd_bwd_ex, and n_correct.  If
+ * `grad_logits` is not NULL it receives d loss / d z = w_i (softmax(z_i) -
+ * onehot) (w_i: reduction scale x grad_scale x grad_rows[i]; 0 on ignored
+ * rows) in dtype, row stride `ld_grad` (same rules; the columns from V up to
+ * the next multiple of 16 bytes are set to 0, the rest of the row is not
+ * written); it may be `logits` itself (then ld_grad must equal ld_logits).
+ * `workspace`: 256-byte aligned, at least flce_cross_entropy_workspace_size(N)
+ * bytes; flce_read_status reports FLCE_ELABEL for out-of-range labels.
+ */
+int flce_cross_entropy(const void* logits, int64_t ld_logits, const int64_t* labels,
+                       int64_t N, int64_t V, int64_t ignore_index, int reduction,
+                       float* loss, int64_t* n_correct, void* grad_logits, int64_t ld_grad,
+                       hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes,
+                       const flce_options_t* options);
+
+/*
  * Synchronise `stream` and return the device-side status of the last
- * flce_fwd_bwd, flce_fwd_bwd_ex or flce_fwd that used `workspace`: FLCE_OK or FLCE_ELABEL.  Returns
+ * flce_fwd_bwd, flce_fwd_bwd_ex, flce_fwd or flce_cross_entropy that used
+ * `workspace`: FLCE_OK or FLCE_ELABEL.  Returns
  * FLCE_EINVAL for a null workspace and FLCE_EDEVICE if the copy fails.
  */
 int flce_read_status(const void* workspace, hipStream_t stream);

@@ -24,10 +24,13 @@ from ._lib import (  # noqa: F401
     FLCE_REDUCTION_SUM,
     KERNEL_KINDS,
     FlceError,
+    flce_cross_entropy,
+    flce_cross_entropy_workspace_size,
     flce_fwd,
     flce_fwd_bwd,
     flce_fwd_bwd_ex,
     flce_fwd_workspace_size,
+    flce_logits,
     flce_options_t,
     flce_profile_enable,
     flce_profile_read,
@@ -36,4 +39,13 @@ from ._lib import (  # noqa: F401
     flce_strerror,
     flce_workspace_size,
 )
-from .torch_api import FlceForward, FlceOutputs, forward, fwd_bwd, linear_cross_entropy  # noqa: F401
+from .torch_api import (  # noqa: F401
+    CrossEntropyOutputs,
+    FlceForward,
+    FlceOutputs,
+    cross_entropy,
+    forward,
+    fwd_bwd,
+    linear_cross_entropy,
+    logits,
+)

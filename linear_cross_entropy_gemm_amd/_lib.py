@@ -28,7 +28,8 @@ FLCE_EUNSUPPORTED = 5
 
 # Every symbol include/flce.h declares.
 EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_fwd_bwd_ex", "flce_fwd_workspace_size",
-            "flce_fwd", "flce_read_status", "flce_strerror", "flce_profile_enable", "flce_profile_read")
+            "flce_fwd", "flce_logits", "flce_cross_entropy_workspace_size", "flce_cross_entropy",
+            "flce_read_status", "flce_strerror", "flce_profile_enable", "flce_profile_read")
 
 # Kernel kinds of the per-kernel timing facility (index order of the arrays).
 KERNEL_KINDS = ("label_scan", "fwd_logits", "row_merge", "grad_logits", "grad_h", "grad_h_reduce",
@@ -90,6 +91,13 @@ def _load() -> ctypes.CDLL:
     lib.flce_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
                              vp, vp, vp, i32, vp, sz, ctypes.POINTER(flce_options_t)]
     lib.flce_fwd.restype = i32
+    lib.flce_logits.argtypes = [vp, vp, i64, i64, i64, f32, f32, vp, i64, vp, i32]
+    lib.flce_logits.restype = i32
+    lib.flce_cross_entropy_workspace_size.argtypes = [i64]
+    lib.flce_cross_entropy_workspace_size.restype = sz
+    lib.flce_cross_entropy.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp, vp, vp, i64, vp, i32, vp, sz,
+                                       ctypes.POINTER(flce_options_t)]
+    lib.flce_cross_entropy.restype = i32
     lib.flce_read_status.argtypes = [vp, vp]
     lib.flce_read_status.restype = i32
     lib.flce_strerror.argtypes = [i32]
@@ -150,6 +158,23 @@ def flce_fwd(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_index: 
     """Raw forward-only call; returns the C return code."""
     return int(_lib.flce_fwd(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
                              loss, n_correct, stream, dtype, workspace, workspace_bytes, _opts(options)))
+
+
+def flce_logits(h: int, W: int, N: int, H: int, V: int, softcap_T: float, multiplier: float, logits: int,
+                ld_logits: int, stream: int, dtype: int) -> int:
+    return int(_lib.flce_logits(h, W, N, H, V, softcap_T, multiplier, logits, ld_logits, stream, dtype))
+
+
+def flce_cross_entropy_workspace_size(N: int) -> int:
+    return int(_lib.flce_cross_entropy_workspace_size(N))
+
+
+def flce_cross_entropy(logits: int, ld_logits: int, labels: int, N: int, V: int, ignore_index: int,
+                       reduction: int, loss: int, n_correct, grad_logits, ld_grad: int, stream: int, dtype: int,
+                       workspace: int, workspace_bytes: int, options) -> int:
+    return int(_lib.flce_cross_entropy(logits, ld_logits, labels, N, V, ignore_index, reduction, loss,
+                                       n_correct, grad_logits, ld_grad, stream, dtype, workspace,
+                                       workspace_bytes, _opts(options)))
 
 
 def flce_read_status(workspace: int, stream: int) -> int:

@@ -58,6 +58,36 @@ __host__ __device__ __forceinline__ float softcap_tanh(float x) {
   return __builtin_fabsf(x) < kTanhSeriesMax ? tanh_series(x) : tanh_exp_form(x);
 }
 
+// Logits of one token block bn of a wave's 4 x 4 accumulator blocks:
+// z = T tanh(m a / T) (kCap) or m a, in place; `scale` is m / T (kCap) or m.
+// The series serves when every lane's |m a / T| < 1/4 (the usual case for
+// lm_head logits under a large cap); otherwise the whole wave takes the
+// exponential form.
+template <bool kCap>
+__device__ __forceinline__ void softcap_block(f32x16 (&acc)[4][4], int bn, float scale, float T) {
+  bool need = false;
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc[bm][bn][v] *= scale;
+      if (kCap) need |= __builtin_fabsf(acc[bm][bn][v]) >= kTanhSeriesMax;
+    }
+  if (kCap) {
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[bm][bn][v] = T * softcap_tanh(acc[bm][bn][v]);
+    } else {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[bm][bn][v] = T * tanh_series(acc[bm][bn][v]);
+    }
+  }
+}
+
 // Online log-sum-exp / argmax state merge (running max m, sum of exp(z - m),
 // index of the first maximum).  Equal maxima keep the lower index.  An empty
 // state is (-inf, 0, INT_MAX); the merge is branch-free and never forms

@@ -151,6 +151,102 @@ extern "C" int flce_fwd(const void* h, const void* W, const int64_t* labels, int
   return flce::run_call(a, p, stream);
 }
 
+namespace {
+
+// Row stride rules of the materialised path: ld >= V and 16-byte rows.
+bool rows_ok(const void* p, int64_t ld, int64_t V, int64_t es) {
+  return p && aligned(p, 16) && ld >= V && (ld * es) % 16 == 0;
+}
+
+int check_shape(int64_t N, int64_t H, int64_t V, int dtype) {
+  // the planner's shape limits (32-bit tile offsets, H alignment)
+  flce::Plan p;
+  const int rc = flce::make_plan(N, H, V, dtype, size_t(1) << 62, true, &p);
+  return rc == FLCE_EWORKSPACE ? FLCE_OK : rc;
+}
+
+}  // namespace
+
+extern "C" int flce_logits(const void* h, const void* W, int64_t N, int64_t H, int64_t V, float softcap_T,
+                           float multiplier, void* logits, int64_t ld_logits, hipStream_t stream, int dtype) {
+  if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
+  if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
+  if (!W || !aligned(W, 16)) return FLCE_EINVAL;
+  if (std::isnan(softcap_T) || std::isinf(softcap_T) || !std::isfinite(multiplier)) return FLCE_EINVAL;
+  const int64_t es = dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  if (N > 0 && (!h || !aligned(h, 16) || !rows_ok(logits, ld_logits, V, es))) return FLCE_EINVAL;
+  int rc = check_shape(N, H, V, dtype);
+  if (rc != FLCE_OK) return rc;
+  if ((int64_t(1) << 31) / 256 <= ld_logits * es) return FLCE_EUNSUPPORTED;
+  flce::LogitsCallArgs a;
+  a.h = h;
+  a.W = W;
+  a.N = N;
+  a.H = H;
+  a.V = V;
+  a.softcap_T = softcap_T;
+  a.multiplier = multiplier;
+  a.out = logits;
+  a.ld_out = ld_logits;
+  a.dtype = dtype;
+  return flce::run_logits(a, stream);
+}
+
+extern "C" size_t flce_cross_entropy_workspace_size(int64_t N) {
+  return N < 0 ? 0 : flce::cross_entropy_workspace(N);
+}
+
+extern "C" int flce_cross_entropy(const void* logits, int64_t ld_logits, const int64_t* labels, int64_t N,
+                                  int64_t V, int64_t ignore_index, int reduction, float* loss,
+                                  int64_t* n_correct, void* grad_logits, int64_t ld_grad, hipStream_t stream,
+                                  int dtype, void* workspace, size_t workspace_bytes,
+                                  const flce_options_t* o) {
+  if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM && reduction != FLCE_REDUCTION_NONE)
+    return FLCE_EINVAL;
+  if (N < 0 || V < 1 || V > (int64_t(1) << 30)) return FLCE_EINVAL;
+  if (N > (int64_t(1) << 31) - 1) return FLCE_EUNSUPPORTED;
+  if (!loss || !aligned(loss, 4) || !workspace || !aligned(workspace, 256)) return FLCE_EINVAL;
+  if (n_correct && !aligned(n_correct, 8)) return FLCE_EINVAL;
+  const int64_t es = dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  if (N > 0) {
+    if (!labels || !aligned(labels, 8) || !rows_ok(logits, ld_logits, V, es)) return FLCE_EINVAL;
+    if (grad_logits && !rows_ok(grad_logits, ld_grad, V, es)) return FLCE_EINVAL;
+    if (grad_logits == logits && ld_grad != ld_logits) return FLCE_EINVAL;
+  }
+  if (reduction == FLCE_REDUCTION_NONE && (!o || !o->loss_rows)) return FLCE_EINVAL;
+  if (o) {
+    if (o->loss_rows && !aligned(o->loss_rows, 4)) return FLCE_EINVAL;
+    if (o->lse_rows && !aligned(o->lse_rows, 4)) return FLCE_EINVAL;
+    if (o->pred_rows && !aligned(o->pred_rows, 8)) return FLCE_EINVAL;
+    if (o->grad_rows && (reduction != FLCE_REDUCTION_NONE || !aligned(o->grad_rows, 4))) return FLCE_EINVAL;
+    if (!std::isfinite(o->grad_scale)) return FLCE_EINVAL;
+  }
+  if (workspace_bytes < flce::cross_entropy_workspace(N)) return FLCE_EWORKSPACE;
+  flce::CeCallArgs a;
+  a.logits = logits;
+  a.ld_logits = ld_logits;
+  a.labels = labels;
+  a.N = N;
+  a.V = V;
+  a.ignore_index = ignore_index;
+  a.reduction = reduction;
+  a.dtype = dtype;
+  a.loss = loss;
+  a.n_correct = n_correct;
+  a.grad = grad_logits;
+  a.ld_grad = ld_grad;
+  a.workspace = workspace;
+  if (o) {
+    a.loss_rows = o->loss_rows;
+    a.lse_rows = o->lse_rows;
+    a.pred_rows = o->pred_rows;
+    a.grad_rows = o->grad_rows;
+    a.grad_scale = o->grad_scale == 0.0f ? 1.0f : o->grad_scale;
+  }
+  return flce::run_cross_entropy(a, stream);
+}
+
 extern "C" int flce_read_status(const void* workspace, hipStream_t stream) {
   if (!workspace) return FLCE_EINVAL;
   flce::Header hdr;

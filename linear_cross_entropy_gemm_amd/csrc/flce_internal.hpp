@@ -61,6 +61,38 @@ struct CallArgs {
 // Enqueue the whole call on `stream`.  Returns FLCE_OK or FLCE_EDEVICE.
 int run_call(const CallArgs& a, const Plan& pl, hipStream_t stream);
 
+// Materialised-logits path (flce_logits / flce_cross_entropy).
+struct LogitsCallArgs {
+  const void* h;
+  const void* W;
+  int64_t N, H, V;
+  float softcap_T, multiplier;
+  void* out;
+  int64_t ld_out;   // elements
+  int dtype;
+};
+int run_logits(const LogitsCallArgs& a, hipStream_t stream);
+
+struct CeCallArgs {
+  const void* logits;
+  int64_t ld_logits;   // elements
+  const int64_t* labels;
+  int64_t N, V, ignore_index;
+  int reduction, dtype;
+  float* loss;
+  int64_t* n_correct;
+  void* grad;          // may alias logits; null: no gradient
+  int64_t ld_grad;     // elements
+  void* workspace;
+  float* loss_rows = nullptr;
+  float* lse_rows = nullptr;
+  int64_t* pred_rows = nullptr;
+  const float* grad_rows = nullptr;
+  float grad_scale = 1.0f;
+};
+int run_cross_entropy(const CeCallArgs& a, hipStream_t stream);
+size_t cross_entropy_workspace(int64_t N);
+
 // Brackets one kernel launch with timing events when profiling is enabled.
 class ProfileScope {
  public:

@@ -162,6 +162,88 @@ def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     return res
 
 
+def _padded_cols(V: int, dtype: torch.dtype) -> int:
+    per = 16 // torch.tensor([], dtype=dtype).element_size()
+    return (V + per - 1) // per * per
+
+
+def logits(h: torch.Tensor, W: torch.Tensor, softcap: Optional[float] = None, multiplier: float = 1.0,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Materialised logits z = cap(m h W^T) (``flce_logits``), [..., V] in
+    the dtype of h.  The rows of the returned tensor have a stride padded to
+    16 bytes (a view of a [N, ld] buffer) when V is not a multiple of 8 (bf16)
+    or 4 (fp32)."""
+    if h.dtype not in _DTYPES or W.dtype != h.dtype:
+        raise TypeError(f"h and W must both be bfloat16 or float32 (got {h.dtype}, {W.dtype})")
+    H = h.shape[-1]
+    h2 = h.reshape(-1, H).contiguous()
+    Wc = W.contiguous()
+    N, V = h2.shape[0], Wc.shape[0]
+    ld = _padded_cols(V, h.dtype)
+    if out is None:
+        out = torch.empty((N, ld), dtype=h.dtype, device=h.device)
+    if out.shape[0] != N or out.stride(1) != 1 or out.stride(0) < V:
+        raise ValueError("out must be [N, ld >= V] with unit column stride")
+    stream = torch.cuda.current_stream(h.device).cuda_stream
+    rc = _lib.flce_logits(_ptr(h2), _ptr(Wc), N, H, V, float(softcap) if softcap else 0.0, float(multiplier),
+                          _ptr(out), out.stride(0), stream, _DTYPES[h.dtype])
+    if rc != _lib.FLCE_OK:
+        raise _lib.FlceError(rc, "flce_logits")
+    return out[:, :V].reshape(*h.shape[:-1], V)
+
+
+@dataclasses.dataclass
+class CrossEntropyOutputs:
+    loss: torch.Tensor
+    n_correct: torch.Tensor
+    workspace: torch.Tensor
+    grad_logits: Optional[torch.Tensor] = None
+    loss_rows: Optional[torch.Tensor] = None
+    lse_rows: Optional[torch.Tensor] = None
+    pred_rows: Optional[torch.Tensor] = None
+
+
+def cross_entropy(z: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
+                  grad: bool = False, in_place: bool = False, grad_rows: Optional[torch.Tensor] = None,
+                  grad_scale: float = 1.0, row_outputs: bool = False, check: bool = True) -> CrossEntropyOutputs:
+    """Cross-entropy of given logits ``z`` [N, V] (``flce_cross_entropy``),
+    optionally with d loss / d z (written into z itself with ``in_place``).
+    z may be a row-padded view (row stride a multiple of 16 bytes)."""
+    if z.dim() != 2 or z.stride(1) != 1 or z.dtype not in _DTYPES:
+        raise ValueError("z must be a [N, V] bfloat16 / float32 tensor with unit column stride")
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    N, V = z.shape
+    lab = labels.reshape(-1).to(torch.int64).contiguous()
+    dev = z.device
+    ws_bytes = _lib.flce_cross_entropy_workspace_size(N)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    res = CrossEntropyOutputs(loss=torch.empty((), dtype=torch.float32, device=dev),
+                              n_correct=torch.empty((), dtype=torch.int64, device=dev), workspace=ws)
+    g = None
+    if grad:
+        g = z if in_place else torch.empty((N, z.stride(0)), dtype=z.dtype, device=dev)
+        res.grad_logits = g if in_place else g[:, :V]
+    want_rows = row_outputs or reduction == "none"
+    res.loss_rows, res.lse_rows, res.pred_rows = _row_buffers(N, dev, want_rows)
+    gr = None
+    if grad_rows is not None:
+        gr = grad_rows.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
+    opts = _lib.flce_options_t(loss_rows=_ptr(res.loss_rows), lse_rows=_ptr(res.lse_rows),
+                               pred_rows=_ptr(res.pred_rows), grad_rows=_ptr(gr), grad_scale=float(grad_scale))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = _lib.flce_cross_entropy(_ptr(z), z.stride(0), _ptr(lab), N, V, int(ignore_index), _REDUCTIONS[reduction],
+                                 _ptr(res.loss), _ptr(res.n_correct), _ptr(g), g.stride(0) if g is not None else 0,
+                                 stream, _DTYPES[z.dtype], _ptr(ws), ws_bytes, opts)
+    if rc != _lib.FLCE_OK:
+        raise _lib.FlceError(rc, "flce_cross_entropy")
+    if check:
+        st = _lib.flce_read_status(_ptr(ws), stream)
+        if st != _lib.FLCE_OK:
+            raise _lib.FlceError(st, "flce_cross_entropy (device status)")
+    return res
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
     """mean / sum: the gradients come out of the fused forward call and are
     scaled by the upstream scalar in backward.  none: the forward computes the

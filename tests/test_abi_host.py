@@ -219,5 +219,68 @@ def test_forward_only_plan_is_smaller_and_unchunked():
     assert L.flce_fwd_workspace_size(4, 12, 8, 0) == 0          # unsupported H
 
 
+def _call_logits(**kw):
+    # base: H = 12 is unsupported for bf16 and is checked last, so no variant
+    # (all with fake addresses) can reach a launch
+    args = dict(h=16, W=16, N=4, H=12, V=8, softcap_T=0.0, multiplier=1.0, logits=256, ld_logits=8,
+                stream=0, dtype=0)
+    args.update(kw)
+    return L.flce_logits(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), L.FLCE_EINVAL),
+    (dict(N=-1), L.FLCE_EINVAL),
+    (dict(V=0), L.FLCE_EINVAL),
+    (dict(W=None), L.FLCE_EINVAL),
+    (dict(W=8), L.FLCE_EINVAL),
+    (dict(h=None), L.FLCE_EINVAL),
+    (dict(logits=None), L.FLCE_EINVAL),
+    (dict(logits=264), L.FLCE_EINVAL),          # misaligned
+    (dict(ld_logits=7), L.FLCE_EINVAL),         # ld < V
+    (dict(ld_logits=12), L.FLCE_EINVAL),        # 24-byte rows
+    (dict(softcap_T=float("nan")), L.FLCE_EINVAL),
+    (dict(), L.FLCE_EUNSUPPORTED),
+])
+def test_logits_rejects_before_launch(kw, code):
+    assert _call_logits(**kw) == code
+
+
+def _call_ce(opts=None, **kw):
+    args = dict(logits=256, ld_logits=8, labels=8, N=4, V=8, ignore_index=-100, reduction=0, loss=4,
+                n_correct=None, grad_logits=None, ld_grad=8, stream=0, dtype=0, workspace=256,
+                workspace_bytes=64)
+    args.update(kw)
+    return L.flce_cross_entropy(*args.values(), opts)
+
+
+@pytest.mark.parametrize("opts,kw,code", [
+    (None, dict(dtype=2), L.FLCE_EINVAL),
+    (None, dict(reduction=3), L.FLCE_EINVAL),
+    (None, dict(reduction=2), L.FLCE_EINVAL),          # none without loss_rows
+    (None, dict(N=-1), L.FLCE_EINVAL),
+    (None, dict(loss=None), L.FLCE_EINVAL),
+    (None, dict(workspace=None), L.FLCE_EINVAL),
+    (None, dict(logits=None), L.FLCE_EINVAL),
+    (None, dict(labels=12), L.FLCE_EINVAL),
+    (None, dict(ld_logits=4), L.FLCE_EINVAL),
+    (None, dict(grad_logits=512, ld_grad=12), L.FLCE_EINVAL),
+    (None, dict(grad_logits=256, ld_grad=16, ld_logits=8), L.FLCE_EINVAL),   # in place needs equal ld
+    (_opts(grad_rows=64), {}, L.FLCE_EINVAL),
+    (_opts(grad_scale=float("inf")), {}, L.FLCE_EINVAL),
+    (None, {}, L.FLCE_EWORKSPACE),
+    (_opts(loss_rows=64, grad_rows=64), dict(reduction=2, grad_logits=256), L.FLCE_EWORKSPACE),
+])
+def test_cross_entropy_rejects_before_launch(opts, kw, code):
+    assert _call_ce(opts, **kw) == code
+
+
+def test_cross_entropy_workspace_size():
+    assert L.flce_cross_entropy_workspace_size(0) == 256
+    assert L.flce_cross_entropy_workspace_size(1) == 256 + 3 * 256
+    assert L.flce_cross_entropy_workspace_size(8192) == 256 + 3 * 8192 * 4
+    assert L.flce_cross_entropy_workspace_size(-1) == 0
+
+
 def test_read_status_null():
     assert L.flce_read_status(None, 0) == L.FLCE_EINVAL

@@ -13,7 +13,10 @@ Per workload (c2..c5 of ``synth.CONFIGS``):
   every column of grad_W sums to zero up to the first-order effect of the
   bf16 logit/gradient transients;
 * the forward-only entry point (c4, c5): loss, n_correct window and every
-  row's log-sum-exp against the stored oracle values.
+  row's log-sum-exp against the stored oracle values;
+* the materialised-logits path at c4 (3.3 GB of bf16 logits, then the
+  cross-entropy kernel): loss and n_correct window against the stored oracle
+  values.
 """
 import os
 
@@ -115,4 +118,25 @@ def test_full_size_forward_only(name):
     log(f"[full] forward only {name}: loss rel {e:.2e}, max row lse rel {e_lse:.2e}, n_correct {nc} in [{lo}, {hi}]")
     assert e <= 2e-3
     assert e_lse <= 2e-3
+    assert lo <= nc <= hi
+
+
+def test_full_size_materialised_c4():
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    cfg = synth.CONFIGS["c4"]
+    gold = np.load(os.path.join(GOLDEN, "c4_rowstats.npz"))
+    log(f"[full] materialised c4: N={cfg.N} H={cfg.H} V={cfg.V}")
+    case = synth.make_case(cfg)
+    h, W, lab = to_device(case)
+    z = L.logits(h, W, cfg.softcap_T, cfg.multiplier)
+    o = L.cross_entropy(z, lab, IGN, cfg.reduction)
+    torch.cuda.synchronize()
+    e = abs(o.loss.item() - float(gold["loss"])) / abs(float(gold["loss"]))
+    valid = case.labels != IGN
+    lo, hi = oracle.n_correct_window(gold["pred"], gold["margin"], gold["z_label"], gold["M"],
+                                     case.labels, valid)
+    nc = int(o.n_correct.item())
+    log(f"[full] materialised c4: loss rel {e:.2e}, n_correct {nc} in [{lo}, {hi}]")
+    assert e <= 2e-3
     assert lo <= nc <= hi
