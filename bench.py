@@ -28,9 +28,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FLCE fwd+bwd tokens/sec at V=202048,H=6656 bf16; % of MFMA bf16 peak"
 METRIC_FWD = "FLCE forward-only tokens/sec at V=202048,H=6656 bf16; % of MFMA bf16 peak"
+METRIC_MAT = "materialised logits + cross-entropy forward tokens/sec at V=202048,H=6656 bf16; % of MFMA bf16 peak"
 # MI355X dense MFMA peaks (TFLOP/s).
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-GEMM_KINDS = ("fwd_logits", "grad_h", "grad_W")
+GEMM_KINDS = ("fwd_logits", "grad_h", "grad_W", "logits")
 
 WORKLOAD_TEXT = {
     "c1": "fp32 small: N=256, H=128, V=1024, 10% ignore_index, mean",
@@ -202,9 +203,10 @@ def main() -> int:
                     metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT"),
                     help="write HBM traffic per launch from four rocprofv3 --pmc runs")
     ap.add_argument("--command", default="", help="command text recorded with --summarize-traffic")
-    ap.add_argument("--entry", default="fwd_bwd", choices=("fwd_bwd", "fwd"),
+    ap.add_argument("--entry", default="fwd_bwd", choices=("fwd_bwd", "fwd", "materialised"),
                     help="fwd_bwd (default): flce_fwd_bwd, the headline metric; fwd: the forward-only "
-                         "flce_fwd (loss and n_correct, 2*N*H*V)")
+                         "flce_fwd (loss and n_correct, 2*N*H*V); materialised: flce_logits into an "
+                         "[N, V] buffer then flce_cross_entropy (the non-fused forward)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration()
@@ -242,11 +244,32 @@ def main() -> int:
     log(f"[bench] plan {plan.as_dict()}")
 
     stream = torch.cuda.current_stream(dev)
-    fwd_only = args.entry == "fwd"
-    if fwd_only:
+    fwd_only = args.entry in ("fwd", "materialised")
+    memory = None
+    red = {"mean": L.FLCE_REDUCTION_MEAN, "sum": L.FLCE_REDUCTION_SUM}[cfg.reduction]
+    if args.entry == "materialised":
+        z = L.logits(h, W, softcap, cfg.multiplier)
+        ce = L.cross_entropy(z, lab, synth.IGNORE_INDEX, cfg.reduction)
+        zbase = z.as_strided((cfg.N, z.stride(0)), (z.stride(0), 1))
+        ws = ce.workspace
+        raw_z = (h.data_ptr(), W.data_ptr(), cfg.N, cfg.H, cfg.V, float(softcap or 0.0), float(cfg.multiplier),
+                 z.data_ptr(), z.stride(0), stream.cuda_stream, dtype_code)
+        raw_ce = (z.data_ptr(), z.stride(0), lab.data_ptr(), cfg.N, cfg.V, synth.IGNORE_INDEX, red,
+                  ce.loss.data_ptr(), ce.n_correct.data_ptr(), None, 0, stream.cuda_stream, dtype_code,
+                  ws.data_ptr(), ws.numel(), None)
+
+        def call():
+            rc = L.flce_logits(*raw_z)
+            if rc == L.FLCE_OK:
+                rc = L.flce_cross_entropy(*raw_ce)
+            if rc != L.FLCE_OK:
+                raise L.FlceError(rc, "materialised path")
+        loss_t, nc_t = ce.loss, ce.n_correct
+        memory = {"logits_bytes": zbase.numel() * zbase.element_size(), "workspace_bytes": ws.numel(),
+                  "fused_forward_workspace_bytes": L.flce_fwd_workspace_size(cfg.N, cfg.H, cfg.V, dtype_code)}
+    elif fwd_only:
         f = L.forward(h, W, lab, **kw)                  # allocates outputs + workspace, checks status
         ws = f.workspace
-        red = {"mean": L.FLCE_REDUCTION_MEAN, "sum": L.FLCE_REDUCTION_SUM}[cfg.reduction]
         raw = (h.data_ptr(), W.data_ptr(), lab.data_ptr(), cfg.N, cfg.H, cfg.V, synth.IGNORE_INDEX,
                float(softcap or 0.0), float(cfg.multiplier), red, f.loss.data_ptr(), f.n_correct.data_ptr(),
                stream.cuda_stream, dtype_code, ws.data_ptr(), ws.numel(), None)
@@ -295,14 +318,16 @@ def main() -> int:
                 "flops_per_launch": flops_per_launch, "avg_launch_ms": round(kernels[dom]["avg_ms"], 4)}
 
     result = {
-        "metric": METRIC_FWD if fwd_only else METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "metric": {"fwd": METRIC_FWD, "materialised": METRIC_MAT}.get(args.entry, METRIC),
+        "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "N": cfg.N, "H": cfg.H,
                    "V": cfg.V, "n_valid": cfg.n_valid, "softcap_T": cfg.softcap_T,
                    "multiplier": cfg.multiplier, "reduction": cfg.reduction,
-                   "entry": "flce_fwd" if fwd_only else "flce_fwd_bwd",
+                   "entry": {"fwd": "flce_fwd", "materialised": "flce_logits + flce_cross_entropy"}.get(
+                       args.entry, "flce_fwd_bwd"),
                    "chunk_rows": cfg.N if fwd_only else plan.chunk_rows,
                    "n_chunks": 1 if fwd_only else plan.n_chunks, "split_k": plan.split_k,
                    "parallelism": "single GPU"},
@@ -310,6 +335,8 @@ def main() -> int:
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
         "roofline": roofline,
     }
+    if memory is not None:
+        result["memory"] = memory
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on {args.cpu_tokens} tokens (host cores) ...")
         result["cpu_baseline"] = (cpu_baseline_forward(case, 3 * args.cpu_tokens) if fwd_only

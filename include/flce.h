@@ -271,7 +271,9 @@ enum {
   FLCE_KERNEL_GRAD_W = 6,       /* grad_W GEMM G^T h, fp32 (overwrite, or on top of the stored grad_W) */
   FLCE_KERNEL_FINALIZE = 7,     /* loss scalar and n_correct */
   FLCE_KERNEL_ZERO = 8,         /* zero grad_W when N = 0 */
-  FLCE_KERNEL_KINDS = 9
+  FLCE_KERNEL_LOGITS = 9,       /* flce_logits: logits GEMM + softcap into the caller's buffer */
+  FLCE_KERNEL_CROSS_ENTROPY = 10,/* flce_cross_entropy: per-row statistics (+ logit gradient) */
+  FLCE_KERNEL_KINDS = 11
 };
 
 /* Turn event timing on (on != 0) or off for subsequent calls.  Returns FLCE_OK. */

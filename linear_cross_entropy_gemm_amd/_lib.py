@@ -33,7 +33,7 @@ EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_fwd_bwd_ex
 
 # Kernel kinds of the per-kernel timing facility (index order of the arrays).
 KERNEL_KINDS = ("label_scan", "fwd_logits", "row_merge", "grad_logits", "grad_h", "grad_h_reduce",
-                "grad_W", "finalize", "zero")
+                "grad_W", "finalize", "zero", "logits", "cross_entropy")
 
 
 class flce_plan_t(ctypes.Structure):

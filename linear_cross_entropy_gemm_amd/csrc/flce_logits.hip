@@ -200,7 +200,7 @@ static int logits_typed(const LogitsCallArgs& a, hipStream_t st) {
   p.out = a.out; p.ldo = a.ld_out * es;
   p.map = TileMap{tiles_voc, tiles_tok, 1, 1, 0, 0};
   if (a.N > 0) {
-    ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
+    ProfileScope ps(FLCE_KERNEL_LOGITS, st);
     logits_kernel<T><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(p);
   }
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_EDEVICE;
@@ -235,7 +235,7 @@ static int ce_typed(const CeCallArgs& a, hipStream_t st) {
     p.grad_scale = a.grad_scale; p.grad_rows = a.grad_rows;
     p.grad = a.grad; p.ldg = a.ld_grad * Elem<T>::size;
     p.lse = lse; p.loss_row = loss_row; p.pred = pred;
-    ProfileScope ps(FLCE_KERNEL_GRAD_LOGITS, st);
+    ProfileScope ps(FLCE_KERNEL_CROSS_ENTROPY, st);
     ce_rows_kernel<T><<<(unsigned)a.N, 256, 0, st>>>(p);
   }
   FinalizeArgs fa;

@@ -28,6 +28,15 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_kernel_kinds_match_the_header():
+    import re
+    text = open(os.path.join(ROOT, "include", "flce.h")).read()
+    kinds = dict((name.lower(), int(v)) for name, v in re.findall(r"FLCE_KERNEL_(\w+)\s*=\s*(\d+)", text))
+    n = kinds.pop("kinds")
+    assert n == len(L.KERNEL_KINDS)
+    assert [k for k, _ in sorted(kinds.items(), key=lambda kv: kv[1])] == [k.lower() for k in L.KERNEL_KINDS]
+
+
 def test_strerror():
     for code in range(6):
         assert L.flce_strerror(code) and L.flce_strerror(code) != "unknown error code"
