@@ -21,7 +21,10 @@ HEADERS = ["device_common.hpp", "gemm_tile.hpp", "flce_internal.hpp", "kernel_ar
 ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code (the compiler would
 # otherwise form v_pk_* from plain float code).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# -packed-fp32-ops: no packed fp32 VALU; -ffp-contract=off: the kernels spell
+# out every fused multiply-add, so the same expression rounds the same way in
+# every instantiation (the forward-only entry reproduces the full call bitwise)
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=off"]
 
 
 def hipcc() -> str:

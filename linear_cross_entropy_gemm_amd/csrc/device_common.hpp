@@ -36,17 +36,17 @@ __device__ __forceinline__ float fast_exp(float x) {
 __host__ __device__ __forceinline__ float tanh_series(float x) {
   const float x2 = x * x;
   float p = 62.0f / 2835.0f;
-  p = p * x2 - 17.0f / 315.0f;
-  p = p * x2 + 2.0f / 15.0f;
-  p = p * x2 - 1.0f / 3.0f;
+  p = __builtin_fmaf(p, x2, -17.0f / 315.0f);
+  p = __builtin_fmaf(p, x2, 2.0f / 15.0f);
+  p = __builtin_fmaf(p, x2, -1.0f / 3.0f);
   p = p * x2;
-  return x + x * p;
+  return __builtin_fmaf(x, p, x);
 }
 __host__ __device__ __forceinline__ float tanh_exp_form(float x) {
   const float ax = __builtin_fabsf(x);
 #if defined(__HIP_DEVICE_COMPILE__)
   const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * ax);
-  const float r = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  const float r = __builtin_fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
 #else
   const float e = __builtin_exp2f(2.0f * kLog2e * ax);
   const float r = 1.0f - 2.0f / (e + 1.0f);
@@ -95,7 +95,7 @@ __device__ __forceinline__ void softcap_block(f32x16 (&acc)[4][4], int bn, float
 __device__ __forceinline__ void merge_stats(float& m, float& s, int& a, float m2, float s2, int a2) {
   const float M = __builtin_fmaxf(m, m2);
   const float Mr = M == kNegInf ? 0.0f : M;
-  s = s * fast_exp(m - Mr) + s2 * fast_exp(m2 - Mr);
+  s = __builtin_fmaf(s, fast_exp(m - Mr), s2 * fast_exp(m2 - Mr));
   a = (m > m2) ? a : (m2 > m) ? a2 : (a < a2 ? a : a2);
   m = M;
 }

@@ -27,6 +27,11 @@ namespace flce {
 // per 32 x 32 block and 16 of its vocabulary entries, so the row statistics
 // reduce in registers first, then across lanes l and l + 32, then across the
 // two waves that share the tokens.
+//
+// With one wave per SIMD nothing hides the latency of a dependent chain, so
+// the running max / first argmax and the exp-sum keep one independent chain
+// per 32-column block (bm), merged in column order at the end; the label's
+// logit is picked only in waves whose 128 columns hold some lane's label.
 template <typename T, bool kCap, bool kStoreZ>
 __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn,
                                              char* smem) {
@@ -54,26 +59,47 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
     const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
     const bool tok_ok = tok < p.C_this;
     const int64_t lab64 = tok_ok ? p.labels[tok] : -1;
-    const int lab = (lab64 >= 0 && lab64 < p.V) ? (int)lab64 : -1;
-    float mx = kNegInf, zl = 0.0f;
-    int ax = 0x7fffffff;
-    bool found = false;
+    // first maximum: one chain per bm, columns ascending inside each
+    float mxb[4];
+    int axb[4];
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
-        const float x = acc[bm][bn][v];
-        // columns visit in increasing order: strict > keeps the first maximum
-        const bool gt = x > mx;
-        mx = gt ? x : mx;
-        ax = gt ? col : ax;
-        const bool is_lab = col == lab;
-        zl = is_lab ? x : zl;
-        found |= is_lab;
-      }
+      mxb[bm] = kNegInf;
+      axb[bm] = 0x7fffffff;
     }
-    if (found) p.zlab[tok] = zl;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+        const float x = acc[bm][bn][v];
+        const bool gt = x > mxb[bm];
+        mxb[bm] = gt ? x : mxb[bm];
+        axb[bm] = gt ? vbase + bm * 32 + 8 * (v >> 2) + (v & 3) : axb[bm];
+      }
+    float mx = mxb[0];
+    int ax = axb[0];
+#pragma unroll
+    for (int bm = 1; bm < 4; ++bm) {   // later blocks hold higher columns: strict >
+      const bool gt = mxb[bm] > mx;
+      mx = gt ? mxb[bm] : mx;
+      ax = gt ? axb[bm] : ax;
+    }
+    // the label's logit, in the rare waves whose columns hold a label
+    const int64_t d64 = lab64 - (int64_t)(tm * kTile + wm * 128);
+    if (__builtin_amdgcn_ballot_w64(d64 >= 0 && d64 < 128)) {
+      const int d = (int)d64 - hi * 4;   // offset from this lane's first column
+      float zl = 0.0f;
+      bool found = false;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const bool is_lab = d == bm * 32 + 8 * (v >> 2) + (v & 3);
+          zl = is_lab ? acc[bm][bn][v] : zl;
+          found |= is_lab;
+        }
+      if (found && lab64 < p.V) p.zlab[tok] = zl;
+    }
     if (kStoreZ && tok_ok) {
       T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + (int64_t)tok * p.ldz);
 #pragma unroll
@@ -83,12 +109,15 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
           store4(zr + vbase + bm * 32 + 8 * i, acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1],
                  acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]);
     }
-    float s = 0.0f;
+    // sum of exp(z - max): one partial sum per bm
     const float mref = mx == kNegInf ? 0.0f : mx;
+    const float off = -mref * kLog2e;
+    float sb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
+    for (int v = 0; v < 16; ++v)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s += fast_exp(acc[bm][bn][v] - mref);
+      for (int bm = 0; bm < 4; ++bm) sb[bm] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bm][bn][v], kLog2e, off));
+    float s = (sb[0] + sb[1]) + (sb[2] + sb[3]);
     const float m2 = __shfl_xor(mx, 32);
     const float s2 = __shfl_xor(s, 32);
     const int a2 = __shfl_xor(ax, 32);
@@ -109,7 +138,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
       red_a[idx] = bidx[bn];
     }
   }
-  __syncthreads();
+  // publishes the LDS partials without waiting for this work-group's z stores
+  lds_barrier();
   if (wm == 0 && hi == 0) {
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn) {
@@ -216,7 +246,7 @@ __global__ __launch_bounds__(256) void grad_logits_kernel(GradLogitArgs p) {
       float d = fast_exp(z - l) - ((int64_t)v == lab ? 1.0f : 0.0f);
       if (p.T > 0.0f) {
         const float u = z * p.invT;
-        d *= 1.0f - u * u;
+        d *= __builtin_fmaf(-u, u, 1.0f);
       }
       g = scale * d;
     }

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(CeArgs p) {
       if (v < p.V) {
         const float x = to_f32(zv[e]);
         if (x > m) {
-          s = s * fast_exp(m - x) + 1.0f;
+          s = __builtin_fmaf(s, fast_exp(m - x), 1.0f);
           m = x;
           a = v;
         } else {

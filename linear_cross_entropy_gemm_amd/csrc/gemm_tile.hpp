@@ -574,6 +574,13 @@ struct MNMajorDirect {
 // after which other waves refill the stage this wave has just read.
 #define FLCE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
 
+// Workgroup barrier that publishes this wave's LDS writes but, unlike
+// __syncthreads, does not wait for its outstanding global stores.  The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Marks every accumulator as used here.  When the accumulators were loaded
 // from memory, the compiler's own wait for those loads lands on this point
 // (one wait per tile) instead of on the first MFMA inside the K loop, where
