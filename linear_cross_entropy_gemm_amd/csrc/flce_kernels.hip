@@ -311,6 +311,43 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Store one wave's 128 x 128 fp32 accumulator quadrant of grad_W^T (M =
+// hidden, N = vocabulary) to the rows of grad_W through LDS, so that every
+// store instruction writes whole 256-byte row segments (in the accumulator
+// layout a store touches 32 rows, 32 bytes each).  The quadrant goes in two
+// halves of 64 hidden values through this wave's own 32 KB of LDS, laid out
+// [128 vocabulary rows][16 units of 16 bytes] with unit u of row r at
+// u ^ (r & 15), so that both the scattered writes and the row reads hit 16
+// distinct 16-byte bank units per 16 lanes.  Wave-local: no barrier.
+__device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], float* gW, int64_t H, int V,
+                                                  int n_base, int m_base, char* lds) {
+  const int lane = threadIdx.x & 63, lo = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int bml = 0; bml < 2; ++bml)
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = bn * 32 + lo;
+          const int unit = bml * 8 + 2 * i + hi;
+          const f32x16& a = acc[2 * half + bml][bn];
+          *reinterpret_cast<f32x4*>(lds + row * 256 + ((unit ^ (row & 15)) << 4)) =
+              f32x4{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+        }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int row = 4 * k + (lane >> 4), u = lane & 15;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(lds + row * 256 + ((u ^ (row & 15)) << 4));
+      const int n = n_base + row, m = m_base + half * 64 + 4 * u;
+      // H is a multiple of 4, so m < H keeps the whole vector inside the row
+      if (n < V && m < H) *reinterpret_cast<f32x4*>(gW + (int64_t)n * H + m) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // grad_W (+)= G^T h_c, computed as its transpose h_c^T G: rows = hidden (M),
 // cols = vocabulary (N), K = tokens.  Both operands are stored with K as the
 // slow dimension and are transposed through registers.  With hidden on the M
@@ -371,15 +408,8 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
     constexpr int bk = kKBytes / Elem<T>::size;
     gemm_mainloop<T>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
   }
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (vec_ok(bm, bn, i))
-          *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(tile0) + voff(bm, bn, i)) =
-              f32x4{acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1], acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]};
+  // the K loop ended with a barrier: the LDS is free, 32 KB per wave
+  store_grad_W_rows(acc, p.gW, p.H, p.V, tn * kTile + wn * 128, tm * kTile + wm * 128, smem + wave * 32768);
 }
 
 // ---------------------------------------------------------------------------
