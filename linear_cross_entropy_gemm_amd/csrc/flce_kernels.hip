@@ -319,11 +319,23 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
 // [128 vocabulary rows][16 units of 16 bytes] with unit u of row r at
 // u ^ (r & 15), so that both the scattered writes and the row reads hit 16
 // distinct 16-byte bank units per 16 lanes.  Wave-local: no barrier.
+// kAccumulate adds the stored grad_W: those loads are row segments too, issued
+// before the half goes through LDS so that their latency overlaps it.
+template <bool kAccumulate>
 __device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], float* gW, int64_t H, int V,
                                                   int n_base, int m_base, char* lds) {
   const int lane = threadIdx.x & 63, lo = lane & 31, hi = lane >> 5;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    f32x4 old[32];
+    if constexpr (kAccumulate) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int n = n_base + 4 * k + (lane >> 4), m = m_base + half * 64 + 4 * (lane & 15);
+        old[k] = (n < V && m < H) ? *reinterpret_cast<const f32x4*>(gW + (int64_t)n * H + m)
+                                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
 #pragma unroll
     for (int bml = 0; bml < 2; ++bml)
 #pragma unroll
@@ -339,7 +351,8 @@ __device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], flo
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const int row = 4 * k + (lane >> 4), u = lane & 15;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(lds + row * 256 + ((u ^ (row & 15)) << 4));
+      f32x4 v = *reinterpret_cast<const f32x4*>(lds + row * 256 + ((u ^ (row & 15)) << 4));
+      if constexpr (kAccumulate) v += old[k];
       const int n = n_base + row, m = m_base + half * 64 + 4 * u;
       // H is a multiple of 4, so m < H keeps the whole vector inside the row
       if (n < V && m < H) *reinterpret_cast<f32x4*>(gW + (int64_t)n * H + m) = v;
@@ -353,54 +366,23 @@ __device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], flo
 // slow dimension and are transposed through registers.  With hidden on the M
 // side each lane owns 4 consecutive hidden entries of one vocabulary row of
 // grad_W per accumulator group, so the fp32 epilogue moves 16 bytes per
-// access.  For every chunk after the first (kAccumulate) the accumulators
-// start from the stored grad_W instead of zero, so the epilogue only stores.
+// access.  For every chunk after the first (kAccumulate) the epilogue adds
+// the stored grad_W (read-modify-write in whole row segments).
 template <typename T, bool kAccumulate>
 __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
-  // accumulator element (bm, bn, 4 i .. 4 i + 3): vocabulary row
-  // n0 + 32 bn, hidden entries m0 + 32 bm + 8 i .. + 3; with m a multiple of
-  // 4 and H a multiple of 4, m < H keeps the whole vector inside the row
-  const int n0 = tn * kTile + wn * 128 + lo;
-  const int m0 = tm * kTile + wm * 128 + 4 * hi;
-  auto vec_ok = [&](int bm, int bn, int i) { return n0 + bn * 32 < p.V && m0 + bm * 32 + 8 * i < p.H; };
-  // byte offset of vector (bm, bn, i) from the tile's first element
-  auto voff = [&](int bm, int bn, int i) -> uint32_t {
-    return (uint32_t)((((int64_t)(wn * 128 + lo + bn * 32) * p.H) + wm * 128 + 4 * hi + bm * 32 + 8 * i) * 4);
-  };
-  float* tile0 = p.gW + (int64_t)tn * kTile * p.H + (int64_t)tm * kTile;
+  const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[4][4];
-  if constexpr (kAccumulate) {
-    // The products are added onto the grad_W accumulated so far: its loads
-    // are issued before the first K stages, so they overlap the pipeline fill
-    // instead of stalling the epilogue.  Vectors outside the matrix read as 0.
-    const int64_t rows = (int64_t)(p.V - tn * kTile < kTile ? p.V - tn * kTile : kTile);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc((const char*)tile0, (rows * p.H - (int64_t)tm * kTile) * 4);
-#pragma unroll
-    for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 o = __builtin_bit_cast(f32x4, load16(rs, vec_ok(bm, bn, i) ? voff(bm, bn, i) : kOOB));
-          acc[bm][bn][4 * i] = o[0];
-          acc[bm][bn][4 * i + 1] = o[1];
-          acc[bm][bn][4 * i + 2] = o[2];
-          acc[bm][bn][4 * i + 3] = o[3];
-        }
-  } else {
-    zero_acc(acc);
-  }
+  zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
     MNMajorDirect la, lb;
     la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0, wm * 128, lane);
     lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0, wn * 128, lane);
     constexpr int bk = kDKBytes / 2;
-    gemm_mainloop_direct<kAccumulate>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
+    gemm_mainloop_direct(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
   } else {
     MNMajorLoader<T> la, lb;
     la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);
@@ -409,7 +391,8 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
     gemm_mainloop<T>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
   }
   // the K loop ended with a barrier: the LDS is free, 32 KB per wave
-  store_grad_W_rows(acc, p.gW, p.H, p.V, tn * kTile + wn * 128, tm * kTile + wm * 128, smem + wave * 32768);
+  store_grad_W_rows<kAccumulate>(acc, p.gW, p.H, p.V, tn * kTile + wn * 128, tm * kTile + wm * 128,
+                                 smem + wave * 32768);
 }
 
 // ---------------------------------------------------------------------------

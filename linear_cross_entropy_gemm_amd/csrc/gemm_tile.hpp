@@ -581,18 +581,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Marks every accumulator as used here.  When the accumulators were loaded
-// from memory, the compiler's own wait for those loads lands on this point
-// (one wait per tile) instead of on the first MFMA inside the K loop, where
-// it would drain the load pipeline every step.
-__device__ __forceinline__ void touch_acc(f32x16 (&acc)[4][4]) {
-  asm volatile(""
-               : "+a"(acc[0][0]), "+a"(acc[0][1]), "+a"(acc[0][2]), "+a"(acc[0][3]),
-                 "+a"(acc[1][0]), "+a"(acc[1][1]), "+a"(acc[1][2]), "+a"(acc[1][3]),
-                 "+a"(acc[2][0]), "+a"(acc[2][1]), "+a"(acc[2][2]), "+a"(acc[2][3]),
-                 "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
-}
-
 // K loop of the direct-to-LDS pipeline.  Per K step, four sub-steps of 16
 // MFMAs per wave, each split into 4 block-row groups fenced in program order;
 // alongside each group the next sub-step's fragments are read (B first).
@@ -601,10 +589,9 @@ __device__ __forceinline__ void touch_acc(f32x16 (&acc)[4][4]) {
 // barrier both publishes them and frees the slots of A_t and B_t; the last
 // sub-step then runs from registers while reading sub-step 0 of step t + 1
 // and issuing B_{t+2}.  The products are added to the values `acc` holds on
-// entry; kLoadedAcc says that those were loaded from memory just before the
-// call.  Ends with every load landed and a barrier, after which the LDS may
+// entry.  Ends with every load landed and a barrier, after which the LDS may
 // be reused by the epilogue.
-template <bool kLoadedAcc = false, class LA, class LB>
+template <class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   if (nk <= 0) return;
   auto slot = [&](int q) -> char* { return smem + q * kDOperand; };
@@ -619,7 +606,6 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
   issue_all(lb, 3);
   FLCE_WAIT_VMCNT(2 * kDLoads);
   __syncthreads();
-  if constexpr (kLoadedAcc) touch_acc(acc);
   u32x4 a[2][4], b[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
