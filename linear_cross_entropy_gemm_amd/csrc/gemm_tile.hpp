@@ -462,18 +462,26 @@ __device__ __forceinline__ u32x4s make_rsrc_words(const char* base, int64_t byte
 }
 
 // One direct-to-LDS load: lane l's 16 bytes at byte offset voff of the buffer
-// land at LDS address lds + 16 l (zeros when voff is out of range).  Written
-// as inline assembly so that the compiler does not treat it as an LDS write
-// that every later LDS read must wait for: the K loop orders these loads
-// itself with explicit vmcnt waits and barriers, and waits for all of them
-// (vmcnt(0)) before the LDS is reused.
-__device__ __forceinline__ void lds_dma16(const u32x4s& r, char* lds, uint32_t voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>((FLCE_AS3 char*)lds));
+// land at LDS byte address lds + 16 l (zeros when voff is out of range).
+// `lds` is wave-uniform and built from scalar values only, so M0 is set by
+// one scalar move.  Written as inline assembly so that the compiler does not
+// treat it as an LDS write that every later LDS read must wait for: the K
+// loop orders these loads itself with explicit vmcnt waits and barriers, and
+// waits for all of them (vmcnt(0)) before the LDS is reused.
+__device__ __forceinline__ void lds_dma16(const u32x4s& r, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(r)
+               : "s"(lds), "v"(voff), "s"(r)
                : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ buffer, and this wave's scalar offset of
+// its first 1 KB load destination inside a slot.
+__device__ __forceinline__ uint32_t lds_address(const char* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const FLCE_AS3 char*)p);
+}
+__device__ __forceinline__ uint32_t wave_lds_offset() {
+  return __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * kDLoads * 1024);
 }
 
 __device__ __forceinline__ int kd_offset(int r, int c) {
@@ -484,7 +492,9 @@ __device__ __forceinline__ int kd_offset(int r, int c) {
 // K-major operand [mn][k] (k contiguous, row stride `ld` bytes).
 struct KMajorDirect {
   const char* base;
-  int64_t range0, kpos, k_bytes;
+  int64_t range0;
+  int kpos, k_bytes;   // K bytes per row stay below 2^31 (planner limits)
+  uint32_t lds_wave;
   uint32_t voff[kDLoads];
   int c16[kDLoads];
   int frag[kDSub];   // per-lane fragment offsets of block 0 per sub-step
@@ -496,8 +506,9 @@ struct KMajorDirect {
     rows = rows < 0 ? 0 : (rows > kTile ? kTile : rows);
     base = static_cast<const char*>(base_) + (int64_t)mn0 * ld;
     range0 = (int64_t)rows * ld;
-    kpos = (int64_t)kstep0 * kDKBytes;
-    k_bytes = k_bytes_;
+    kpos = kstep0 * kDKBytes;
+    k_bytes = (int)k_bytes_;
+    lds_wave = wave_lds_offset();
 #pragma unroll
     for (int j = 0; j < kDLoads; ++j) {
       const int B = (w * kDLoads + j) * 4 + (lam >> 4);
@@ -510,11 +521,12 @@ struct KMajorDirect {
 #pragma unroll
     for (int ks = 0; ks < kDSub; ++ks) frag[ks] = kd_offset(row0 + lo, 2 * ks + hi);
   }
-  // Issue this wave's load j of the current K step into `stage`.
-  __device__ __forceinline__ void issue_part(char* stage, int j) {
+  // Issue this wave's load j of the current K step into the slot at LDS
+  // byte address `slot`; chunks past the row's K extent read as zeros.
+  __device__ __forceinline__ void issue_part(uint32_t slot, int j) {
     const u32x4s rs = make_rsrc_words(base + kpos, range0 - kpos);
-    const uint32_t off = kpos + c16[j] < k_bytes ? voff[j] : kOOB;
-    lds_dma16(rs, stage + ((threadIdx.x >> 6) * kDLoads + j) * 1024, off);
+    const uint32_t off = c16[j] < k_bytes - kpos ? voff[j] : kOOB;
+    lds_dma16(rs, slot + lds_wave + j * 1024, off);
   }
   __device__ __forceinline__ void advance() { kpos += kDKBytes; }
   // Fragment of block b (rows row0 + 32 b + (l & 31)) for sub-step ks.
@@ -528,6 +540,7 @@ struct MNMajorDirect {
   const char* base;
   int64_t ld;
   int krow0, k_valid;
+  uint32_t lds_wave;
   uint32_t voff[kDLoads];
   int frag[4];   // per-lane offsets of blocks 0..3 (sub-step 0, first half)
 
@@ -538,6 +551,7 @@ struct MNMajorDirect {
     base = static_cast<const char*>(base_);
     krow0 = kstep0 * (kDKBytes / 2);
     k_valid = k_valid_;
+    lds_wave = wave_lds_offset();
 #pragma unroll
     for (int j = 0; j < kDLoads; ++j) {
       const int kr = (w * kDLoads + j) * 2 + (lam >> 5);
@@ -553,9 +567,9 @@ struct MNMajorDirect {
     for (int b = 0; b < 4; ++b)
       frag[b] = (8 * (g >> 1) + q) * 512 + (((4 * b + x) ^ (4 * q)) << 4) + (p & 1) * 8 + row0 * 2;
   }
-  __device__ __forceinline__ void issue_part(char* stage, int j) {
+  __device__ __forceinline__ void issue_part(uint32_t slot, int j) {
     const u32x4s rs = make_rsrc_words(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
-    lds_dma16(rs, stage + ((threadIdx.x >> 6) * kDLoads + j) * 1024, voff[j]);
+    lds_dma16(rs, slot + lds_wave + j * 1024, voff[j]);
   }
   __device__ __forceinline__ void advance() { krow0 += kDKBytes / 2; }
   __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
@@ -595,9 +609,11 @@ template <class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   if (nk <= 0) return;
   auto slot = [&](int q) -> char* { return smem + q * kDOperand; };
+  const uint32_t smem_lds = lds_address(smem);
+  auto slot_lds = [&](int q) -> uint32_t { return smem_lds + q * kDOperand; };
   auto issue_all = [&](auto& ld, int q) {
 #pragma unroll
-    for (int j = 0; j < kDLoads; ++j) ld.issue_part(slot(q), j);
+    for (int j = 0; j < kDLoads; ++j) ld.issue_part(slot_lds(q), j);
     ld.advance();
   };
   issue_all(la, 0);
@@ -641,11 +657,11 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
           a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
         }
         if (ks == 0) {
-          la.issue_part(slot(sfree), 2 * g);
-          la.issue_part(slot(sfree), 2 * g + 1);
+          la.issue_part(slot_lds(sfree), 2 * g);
+          la.issue_part(slot_lds(sfree), 2 * g + 1);
         } else if (last) {
-          lb.issue_part(slot(sa), 2 * g);
-          lb.issue_part(slot(sa), 2 * g + 1);
+          lb.issue_part(slot_lds(sa), 2 * g);
+          lb.issue_part(slot_lds(sa), 2 * g + 1);
         }
       }
       if (ks == 0) la.advance();
