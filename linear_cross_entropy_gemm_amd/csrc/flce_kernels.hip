@@ -32,6 +32,8 @@ namespace flce {
 // the running max / first argmax and the exp-sum keep one independent chain
 // per 32-column block (bm), merged in column order at the end; the label's
 // logit is picked only in waves whose 128 columns hold some lane's label.
+constexpr int kZStage = 4096;   // LDS byte offset of the z staging buffers (after the row partials)
+
 template <typename T, bool kCap, bool kStoreZ>
 __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn,
                                              char* smem) {
@@ -100,7 +102,30 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
         }
       if (found && lab64 < p.V) p.zlab[tok] = zl;
     }
-    if (kStoreZ && tok_ok) {
+    if constexpr (kStoreZ && sizeof(T) == 2) {
+      // Through this wave's LDS so that each store writes whole 256-byte
+      // row segments: [32 tokens][16 units of 16 bytes], unit u of row r at
+      // u ^ (r & 15).  A lane's 4 values at columns 32 bm + 8 i + 4 hi are
+      // the half hi of unit 4 bm + i.  Wave-local: no barrier.
+      char* zs = smem + kZStage + wave * 32768 + bn * 8192;
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int u = (4 * bm + i) ^ (lo & 15);
+          store4(reinterpret_cast<bf16*>(zs + lo * 256 + (u << 4) + 8 * hi), acc[bm][bn][4 * i],
+                 acc[bm][bn][4 * i + 1], acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]);
+        }
+      const int u = lane & 15;
+      char* zcol = static_cast<char*>(p.z) + (int64_t)(tm * kTile + wm * 128 + 8 * u) * 2;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(zs + r * 256 + ((u ^ (r & 15)) << 4));
+        const int t = tn * kTile + wn * 128 + bn * 32 + r;
+        if (t < p.C_this) *reinterpret_cast<u32x4*>(zcol + (int64_t)t * p.ldz) = w;
+      }
+    } else if (kStoreZ && tok_ok) {
       T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + (int64_t)tok * p.ldz);
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
@@ -285,29 +310,52 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
     lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0);
     gemm_mainloop<T>(la, lb, nk, smem, acc);
   }
+  // The partial keeps the accumulator order: tile (tm, tn) is 64 K floats,
+  // [wave][bm][bn][quad j][lane][4], so every store writes 1 KB contiguous.
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
-  float* out = p.part + (int64_t)sp * p.part_stride;
+  float* out = p.part + (int64_t)sp * p.part_stride + ((int64_t)(tm * p.map.tiles_n + tn) << 16) +
+               wave * 16384 + lane * 4;
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-      const int col = tn * kTile + wn * 128 + bn * 32 + lo;
+    for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = tm * kTile + wm * 128 + bm * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-        if (row < p.C_this && col < p.H) out[(int64_t)row * p.H + col] = acc[bm][bn][v];
+      for (int j = 0; j < 4; ++j) {
+        f32x4 q = {acc[bm][bn][4 * j], acc[bm][bn][4 * j + 1], acc[bm][bn][4 * j + 2], acc[bm][bn][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(out + ((bm * 4 + bn) * 4 + j) * 256) = q;
       }
-    }
 }
 
+// grad_h rows = sum of the split partials, in split order.  One thread per
+// lane group of a tile: its 16 values sit in 4 quads 1 KB apart (the layout
+// grad_h_kernel stores) and map to rows 8 (v >> 2) + 4 hi + (v & 3) of a
+// 32 x 32 block at column lo.
 template <typename T>
 __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= p.n) return;
-  f32x4 a = *reinterpret_cast<const f32x4*>(p.part + i);
-  for (int s = 1; s < p.splits; ++s) a += *reinterpret_cast<const f32x4*>(p.part + s * p.part_stride + i);
-  store4(static_cast<T*>(p.out) + i, a[0], a[1], a[2], a[3]);
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= p.groups) return;
+  const int tile = (int)(g >> 12), r = (int)(g & 4095);
+  const int lane = r & 63, blk = r >> 6;           // blk = (wave * 4 + bm) * 4 + bn
+  const int wave = blk >> 4, bm = (blk >> 2) & 3, bn = blk & 3;
+  const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  const int col = tn * kTile + (wave & 1) * 128 + bn * 32 + (lane & 31);
+  const int row0 = tm * kTile + (wave >> 1) * 128 + bm * 32 + 4 * (lane >> 5);
+  const float* src = p.part + ((int64_t)tile << 16) + blk * 1024 + lane * 4;
+  f32x4 a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const f32x4*>(src + j * 256);
+  for (int s = 1; s < p.splits; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] += *reinterpret_cast<const f32x4*>(src + s * p.part_stride + j * 256);
+  if (col >= p.H) return;
+  T* out = static_cast<T*>(p.out);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + 8 * j + e;
+      if (row < p.C_this) out[(int64_t)row * p.H + col] = (T)a[j][e];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -488,7 +536,8 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gh.ksteps_total = (int)(((int64_t)Vp * es) / kKBytes);
     gh.ksteps_per_split = (gh.ksteps_total + (int)pl.split_k - 1) / (int)pl.split_k;
     const int splits = (gh.ksteps_total + gh.ksteps_per_split - 1) / gh.ksteps_per_split;
-    gh.part = ghpart; gh.part_stride = (int64_t)C * H;
+    const int64_t part_stride = ((int64_t)((C + kTile - 1) / kTile) * tiles_hid) << 16;
+    gh.part = ghpart; gh.part_stride = part_stride;
     gh.map = TileMap{tiles_tok, tiles_hid, splits, tiles_tok, 0, 0};
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_H, st);
@@ -496,12 +545,13 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     }
 
     GradHReduceArgs gr;
-    gr.part = ghpart; gr.part_stride = (int64_t)C * H; gr.splits = splits;
-    gr.n = (int64_t)Ct * H;
+    gr.part = ghpart; gr.part_stride = part_stride; gr.splits = splits;
+    gr.C_this = Ct; gr.H = H; gr.tiles_n = tiles_hid;
+    gr.groups = (int64_t)tiles_tok * tiles_hid * 4096;
     gr.out = static_cast<char*>(a.grad_h) + c0 * a.H * es;
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_H_REDUCE, st);
-      grad_h_reduce_kernel<T><<<grid_1d(gr.n / 4, 256), 256, 0, st>>>(gr);
+      grad_h_reduce_kernel<T><<<grid_1d(gr.groups, 256), 256, 0, st>>>(gr);
     }
 
     GradWArgs gw;

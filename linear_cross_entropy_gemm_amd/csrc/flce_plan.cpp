@@ -69,7 +69,9 @@ void layout(Plan* p) {
     p->off_z = p->off_ghpart = 0;
   } else {
     p->off_z = take(size_t(p->C) * size_t(p->Vp) * size_t(p->es));
-    p->off_ghpart = take(size_t(p->split_k) * size_t(p->C) * size_t(p->H) * 4);
+    // grad_h partials in whole 256 x 256 fp32 tiles (accumulator order)
+    const size_t tiles = size_t((p->C + kRowTile - 1) / kRowTile) * size_t((p->H + 255) / 256);
+    p->off_ghpart = take(size_t(p->split_k) * tiles * 65536 * 4);
   }
   p->total = off;
 }

@@ -68,7 +68,8 @@ struct GradHReduceArgs {
   const float* part;
   int64_t part_stride;
   int splits;
-  int64_t n;
+  int C_this, H, tiles_n;
+  int64_t groups;   // 16-value lane groups: 4096 per 256 x 256 tile
   void* out;
 };
 
