@@ -192,11 +192,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
   f32x16 acc[4][4];
   zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    KMajorDirect la, lb;
-    la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0, (wave >> 1) * 128, lane);
-    lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0, (wave & 1) * 128, lane);
-    gemm_mainloop_direct(la, lb, (int)((kbytes + kDKBytes - 1) / kDKBytes), smem, acc);
+    gemm_kmajor_direct(p.W, p.ldw, tm * kTile, p.V, p.h, p.ldh, tn * kTile, p.C_this, kbytes, smem, acc);
   } else {
     KMajorLoader la, lb;
     la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0);
@@ -298,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
     // the split is planned in 128-byte K steps, the direct pipeline's step
     static_assert(kKBytes == kDKBytes, "one K step per planned step");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    KMajorDirect la;
+    KMajorDirect<false> la;   // rows of Vp elements: whole K steps
     la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, k0, (wave >> 1) * 128, lane);
     MNMajorDirect lb;
     lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0, (wave & 1) * 128, lane);

@@ -86,11 +86,7 @@ __global__ __launch_bounds__(kThreads, 1) void logits_kernel(LogitsArgs p) {
   f32x16 acc[4][4];
   zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    KMajorDirect la, lb;
-    la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0, (wave >> 1) * 128, lane);
-    lb.init(p.h, p.ldh, tn * kTile, p.N, kbytes, 0, (wave & 1) * 128, lane);
-    gemm_mainloop_direct(la, lb, (int)((kbytes + kDKBytes - 1) / kDKBytes), smem, acc);
+    gemm_kmajor_direct(p.W, p.ldw, tm * kTile, p.V, p.h, p.ldh, tn * kTile, p.N, kbytes, smem, acc);
   } else {
     KMajorLoader la, lb;
     la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0);

@@ -461,18 +461,19 @@ __device__ __forceinline__ u32x4s make_rsrc_words(const char* base, int64_t byte
   return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)n, 0x00020000u};
 }
 
-// One direct-to-LDS load: lane l's 16 bytes at byte offset voff of the buffer
-// land at LDS byte address lds + 16 l (zeros when voff is out of range).
-// `lds` is wave-uniform and built from scalar values only, so M0 is set by
-// one scalar move.  Written as inline assembly so that the compiler does not
-// treat it as an LDS write that every later LDS read must wait for: the K
-// loop orders these loads itself with explicit vmcnt waits and barriers, and
-// waits for all of them (vmcnt(0)) before the LDS is reused.
+// One direct-to-LDS load: lane l's 16 bytes at byte offset soff + voff of the
+// buffer land at LDS byte address lds + 16 l (zeros when the offset is out of
+// range).  `lds` is wave-uniform and goes to M0 through the register
+// constraint, so the compiler forms it there with one scalar add.  Written as
+// inline assembly so that the compiler does not treat it as an LDS write that
+// every later LDS read must wait for: the K loop orders these loads itself with
+// explicit vmcnt waits and barriers, and waits for all of them (vmcnt(0))
+// before the LDS is reused.
+__device__ __forceinline__ void lds_dma16(const u32x4s& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
+}
 __device__ __forceinline__ void lds_dma16(const u32x4s& r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(r)
-               : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds) : "memory");
 }
 
 // LDS byte address of a __shared__ buffer, and this wave's scalar offset of
@@ -490,9 +491,12 @@ __device__ __forceinline__ int kd_offset(int r, int c) {
 }
 
 // K-major operand [mn][k] (k contiguous, row stride `ld` bytes).
+// kTail: the K extent may end inside a 128-byte step (rows of H elements
+// with H not a multiple of 64), so each chunk is checked against it.
+template <bool kTail>
 struct KMajorDirect {
-  const char* base;
-  int64_t range0;
+  u32x4s rs;           // the tile's rows; the K position goes in the scalar offset
+  uint32_t range0;     // bytes of the tile's rows
   int kpos, k_bytes;   // K bytes per row stay below 2^31 (planner limits)
   uint32_t lds_wave;
   uint32_t voff[kDLoads];
@@ -504,10 +508,16 @@ struct KMajorDirect {
     const int t = threadIdx.x, w = t >> 6, lam = t & 63;
     int rows = mn_valid - mn0;
     rows = rows < 0 ? 0 : (rows > kTile ? kTile : rows);
-    base = static_cast<const char*>(base_) + (int64_t)mn0 * ld;
-    range0 = (int64_t)rows * ld;
+    // Lanes of rows in range read kpos + voff < rows * ld, inside the tile's
+    // rows, whether or not the range check counts the scalar offset; steps
+    // past the K extent (the pipeline runs two ahead) get no records at all.
+    rs = make_rsrc_words(static_cast<const char*>(base_) + (int64_t)mn0 * ld, (int64_t)rows * ld);
+    range0 = rs[2];
     kpos = kstep0 * kDKBytes;
+    // kept in a scalar register: the offset field takes no literal constants
+    asm volatile("" : "+s"(kpos));
     k_bytes = (int)k_bytes_;
+    set_records();
     lds_wave = wave_lds_offset();
 #pragma unroll
     for (int j = 0; j < kDLoads; ++j) {
@@ -522,13 +532,20 @@ struct KMajorDirect {
     for (int ks = 0; ks < kDSub; ++ks) frag[ks] = kd_offset(row0 + lo, 2 * ks + hi);
   }
   // Issue this wave's load j of the current K step into the slot at LDS
-  // byte address `slot`; chunks past the row's K extent read as zeros.
+  // byte address `slot`; with kTail, chunks past the row's K extent read as
+  // zeros.
   __device__ __forceinline__ void issue_part(uint32_t slot, int j) {
-    const u32x4s rs = make_rsrc_words(base + kpos, range0 - kpos);
-    const uint32_t off = c16[j] < k_bytes - kpos ? voff[j] : kOOB;
-    lds_dma16(rs, slot + lds_wave + j * 1024, off);
+    uint32_t off = voff[j];
+    if constexpr (kTail) off = c16[j] < k_bytes - kpos ? off : kOOB;
+    lds_dma16(rs, slot + lds_wave + j * 1024, off, (uint32_t)kpos);
   }
-  __device__ __forceinline__ void advance() { kpos += kDKBytes; }
+  __device__ __forceinline__ void set_records() {
+    rs[2] = __builtin_amdgcn_readfirstlane(kpos < k_bytes ? range0 : 0u);
+  }
+  __device__ __forceinline__ void advance() {
+    kpos += kDKBytes;
+    set_records();
+  }
   // Fragment of block b (rows row0 + 32 b + (l & 31)) for sub-step ks.
   __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
     return *reinterpret_cast<const u32x4*>(stage + frag[ks] + b * 32 * kDKBytes);
@@ -537,9 +554,10 @@ struct KMajorDirect {
 
 // MN-major operand [k][mn] (mn contiguous, row stride `ld` bytes).
 struct MNMajorDirect {
-  const char* base;
-  int64_t ld;
-  int krow0, k_valid;
+  const char* kbase;   // K row krow0 of the operand
+  int ldb;             // row pitch in bytes; 64 rows of it stay below 2^31
+  int krem;            // K rows left from krow0
+  u32x4s rs;           // this step's rows (none past the K extent)
   uint32_t lds_wave;
   uint32_t voff[kDLoads];
   int frag[4];   // per-lane offsets of blocks 0..3 (sub-step 0, first half)
@@ -547,16 +565,17 @@ struct MNMajorDirect {
   __device__ __forceinline__ void init(const void* base_, int64_t ld_, int mn0, int mn_valid, int k_valid_,
                                        int kstep0, int row0, int lane) {
     const int t = threadIdx.x, w = t >> 6, lam = t & 63;
-    ld = ld_;
-    base = static_cast<const char*>(base_);
-    krow0 = kstep0 * (kDKBytes / 2);
-    k_valid = k_valid_;
+    const int krow0 = kstep0 * (kDKBytes / 2);
+    ldb = (int)ld_;
+    kbase = static_cast<const char*>(base_) + (int64_t)krow0 * ld_;
+    krem = k_valid_ - krow0;
+    set_rsrc();
     lds_wave = wave_lds_offset();
 #pragma unroll
     for (int j = 0; j < kDLoads; ++j) {
       const int kr = (w * kDLoads + j) * 2 + (lam >> 5);
       const int u = (lam & 31) ^ ((kr & 3) << 2);
-      voff[j] = mn0 + 8 * u < mn_valid ? (uint32_t)(kr * ld + (int64_t)(mn0 + 8 * u) * 2) : kOOB;
+      voff[j] = mn0 + 8 * u < mn_valid ? (uint32_t)(kr * ld_ + (int64_t)(mn0 + 8 * u) * 2) : kOOB;
     }
     // lane (g, p): K row 8 (g >> 1) + (p >> 2) (+ 16 ks + 4 half), MN unit
     // row0/8 + 4 b + 2 (g & 1) + ((p & 3) >> 1), byte (p & 1) * 8 of the unit
@@ -567,11 +586,21 @@ struct MNMajorDirect {
     for (int b = 0; b < 4; ++b)
       frag[b] = (8 * (g >> 1) + q) * 512 + (((4 * b + x) ^ (4 * q)) << 4) + (p & 1) * 8 + row0 * 2;
   }
+  // The step's 64 K rows, or the rows left before the K extent (zeros past it).
+  __device__ __forceinline__ void set_rsrc() {
+    const int rows = krem < kDKBytes / 2 ? (krem < 0 ? 0 : krem) : kDKBytes / 2;
+    const uint64_t a = reinterpret_cast<uint64_t>(kbase);
+    rs = u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu,
+                (uint32_t)__builtin_amdgcn_readfirstlane(rows * ldb), 0x00020000u};
+  }
   __device__ __forceinline__ void issue_part(uint32_t slot, int j) {
-    const u32x4s rs = make_rsrc_words(base + (int64_t)krow0 * ld, (int64_t)(k_valid - krow0) * ld);
     lds_dma16(rs, slot + lds_wave + j * 1024, voff[j]);
   }
-  __device__ __forceinline__ void advance() { krow0 += kDKBytes / 2; }
+  __device__ __forceinline__ void advance() {
+    kbase += (int64_t)ldb * (kDKBytes / 2);
+    krem -= kDKBytes / 2;
+    set_rsrc();
+  }
   __device__ __forceinline__ u32x4 read(const char* stage, int b, int ks) const {
     const char* q = stage + frag[b] + ks * 8192;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FLCE_AS3 i16x4*)(q));
@@ -674,6 +703,27 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
   FLCE_FENCE();
   FLCE_WAIT_VMCNT(0);
   __syncthreads();
+}
+
+// Both operands K-major (rows of kbytes bytes): A rows a0.. (of a_valid) on
+// the M side, B rows b0.. (of b_valid) on the N side.  The K tail check is
+// compiled in only when the rows end inside a 128-byte step.
+__device__ __forceinline__ void gemm_kmajor_direct(const void* A, int64_t lda, int a0, int a_valid, const void* B,
+                                                   int64_t ldb, int b0, int b_valid, int64_t kbytes, char* smem,
+                                                   f32x16 (&acc)[4][4]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nk = (int)((kbytes + kDKBytes - 1) / kDKBytes);
+  if (kbytes % kDKBytes == 0) {
+    KMajorDirect<false> la, lb;
+    la.init(A, lda, a0, a_valid, kbytes, 0, (wave >> 1) * 128, lane);
+    lb.init(B, ldb, b0, b_valid, kbytes, 0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, nk, smem, acc);
+  } else {
+    KMajorDirect<true> la, lb;
+    la.init(A, lda, a0, a_valid, kbytes, 0, (wave >> 1) * 128, lane);
+    lb.init(B, ldb, b0, b_valid, kbytes, 0, (wave & 1) * 128, lane);
+    gemm_mainloop_direct(la, lb, nk, smem, acc);
+  }
 }
 
 }  // namespace flce
