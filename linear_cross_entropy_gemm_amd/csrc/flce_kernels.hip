@@ -496,7 +496,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     f.z = a.fwd_only ? nullptr : zbuf; f.ldz = (int64_t)Vp * es;
     f.pmax = pmax; f.psum = psum; f.parg = parg; f.ldp = C;
     f.zlab = zlab + c0;
-    f.map = TileMap{tiles_voc, tiles_tok, 1, 1, 0, 0};
+    f.map = TileMap{tiles_voc, tiles_tok, 1, 4, 1, 0};
     {
       ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
       if (a.fwd_only)
