@@ -74,6 +74,16 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is not built; run `python linear_cross_entropy_gemm_amd/build.py` "
             "(the FLCE path has no fallback implementation)")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7.  If
+    # this library were loaded first, the dynamic linker would map the system
+    # ROCm runtime for it and torch would then load its own second copy;
+    # device pointers and streams of one runtime are not valid in the other,
+    # and every launch fails.  Loading torch first makes this library bind to
+    # torch's runtime (same soname).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, sz, vp, i32, f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.flce_plan.argtypes = [i64, i64, i64, i32, sz, ctypes.POINTER(flce_plan_t)]

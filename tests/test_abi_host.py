@@ -293,3 +293,19 @@ def test_cross_entropy_workspace_size():
 
 def test_read_status_null():
     assert L.flce_read_status(None, 0) == L.FLCE_EINVAL
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not map a second HIP runtime
+    (torch's bundled one plus the system one): pointers and streams of one
+    runtime are invalid in the other.  Runs on the CPU: only the libraries
+    mapped into a fresh process are inspected."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import linear_cross_entropy_gemm_amd\nimport torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    maps = eval(out.stdout.strip().splitlines()[-1])
+    assert len(maps) == 1, maps
