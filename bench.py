@@ -310,12 +310,17 @@ def main() -> int:
             log(f"[bench]   {k:14s} {tot / args.steps:8.3f} ms/step  {n / args.steps:4.1f} launches  "
                 f"{tot / n:8.3f} ms avg")
     dom = max((k for k in kernels if k in GEMM_KINDS), key=lambda k: kernels[k]["ms_per_step"])
-    flops_per_launch = 2.0 * cfg.N * cfg.H * cfg.V / kernels[dom]["launches_per_step"]
+    # The fused entries pack the valid rows before the GEMMs, so their GEMM
+    # launches together process N_valid token rows; the materialised logits
+    # GEMM processes all N.
+    rows_alg = cfg.n_valid if args.entry in ("fwd_bwd", "fwd") else cfg.N
+    flops_per_launch = 2.0 * rows_alg * cfg.H * cfg.V / kernels[dom]["launches_per_step"]
     achieved = flops_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
     traffic = stored_traffic(dom, args.config)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                "flops_per_launch": flops_per_launch, "avg_launch_ms": round(kernels[dom]["avg_ms"], 4)}
+                "flops_per_launch": flops_per_launch, "token_rows_per_launch": rows_alg / kernels[dom]["launches_per_step"],
+                "avg_launch_ms": round(kernels[dom]["avg_ms"], 4)}
 
     result = {
         "metric": {"fwd": METRIC_FWD, "materialised": METRIC_MAT}.get(args.entry, METRIC),

@@ -135,6 +135,14 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t bu
  * N = 0 or no valid row gives loss = 0, n_correct = 0 and zero gradients.
  * Calls on distinct workspaces may run concurrently; two calls sharing a
  * workspace must be ordered (same stream).
+ *
+ * Ignored rows add nothing to the loss or to either gradient, so the call
+ * first packs the valid rows of h (in order) into the workspace and runs the
+ * GEMMs over those alone; the chunks then cover packed rows.  The results are
+ * those of the definition above; only the rounding order of grad_W's sum
+ * over tokens and of the loss sum depends on which rows are packed together.
+ * (flce_fwd_bwd_ex and flce_fwd skip the packing when every row's
+ * log-sum-exp or argmax is requested: those are defined for ignored rows too.)
  */
 int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels,
                  int64_t N, int64_t H, int64_t V,
@@ -262,7 +270,7 @@ const char* flce_strerror(int code);
  * that kernel's own duration on that stream.  Kinds index the arrays below.
  */
 enum {
-  FLCE_KERNEL_LABEL_SCAN = 0,   /* header init + label scan (ignore mask, N_valid, range check) */
+  FLCE_KERNEL_LABEL_SCAN = 0,   /* header init + label scan (N_valid, range check) and valid-row packing */
   FLCE_KERNEL_FWD_LOGITS = 1,   /* logits GEMM + softcap / LSE / argmax / label-logit epilogue */
   FLCE_KERNEL_ROW_MERGE = 2,    /* per-token log-sum-exp, loss, argmax */
   FLCE_KERNEL_GRAD_LOGITS = 3,  /* softmax - onehot (x softcap derivative), in place */

@@ -47,21 +47,38 @@ static __global__ __launch_bounds__(256) void label_scan_kernel(const int64_t* l
 }
 
 // loss = s * sum of the per-row losses (fp64, fixed order; s = 1 for sum and
-// none), n_correct, and the requested per-row outputs.
+// none), n_correct, and the requested per-row outputs.  With valid-row
+// packing the sums run over the packed rows and the per-row losses are
+// scattered back to the caller's rows (0 on ignored rows).
 static __global__ __launch_bounds__(1024) void finalize_kernel(FinalizeArgs p) {
   __shared__ double ls[1024];
   __shared__ long long cs[1024];
   double a = 0.0;
   long long c = 0;
-  for (int64_t i = threadIdx.x; i < p.N; i += 1024) {
-    const int64_t lab = p.labels[i];
-    if (lab != p.ignore_index) {
-      a += (double)p.loss_row[i];
-      c += (p.pred[i] == lab) ? 1 : 0;
+  if (p.ppos) {
+    // packed rows: every one is valid; row outputs other than the loss are
+    // never requested on this path
+    const int64_t nv = (int64_t)p.hdr->n_valid;
+    for (int64_t j = threadIdx.x; j < nv; j += 1024) {
+      a += (double)p.loss_row[j];
+      c += (p.pred[j] == p.plab[j]) ? 1 : 0;
     }
-    if (p.loss_rows) p.loss_rows[i] = p.loss_row[i];
-    if (p.lse_rows) p.lse_rows[i] = p.lse[i];
-    if (p.pred_rows) p.pred_rows[i] = p.pred[i];
+    if (p.loss_rows)
+      for (int64_t i = threadIdx.x; i < p.N; i += 1024) {
+        const int q = p.ppos[i];
+        p.loss_rows[i] = q >= 0 ? p.loss_row[q] : 0.0f;
+      }
+  } else {
+    for (int64_t i = threadIdx.x; i < p.N; i += 1024) {
+      const int64_t lab = p.labels[i];
+      if (lab != p.ignore_index) {
+        a += (double)p.loss_row[i];
+        c += (p.pred[i] == lab) ? 1 : 0;
+      }
+      if (p.loss_rows) p.loss_rows[i] = p.loss_row[i];
+      if (p.lse_rows) p.lse_rows[i] = p.lse[i];
+      if (p.pred_rows) p.pred_rows[i] = p.pred[i];
+    }
   }
   ls[threadIdx.x] = a;
   cs[threadIdx.x] = c;

@@ -30,8 +30,15 @@ struct Plan {
   size_t off_lse, off_zlab, off_loss_row, off_pred;
   size_t off_pmax, off_psum, off_parg;
   size_t off_z, off_ghpart;
+  // valid-row packing: per 1024-row block counts / offsets, packed position
+  // of each row (-1: ignored), original row of each packed row, packed
+  // labels, packed upstream row gradients, packed h rows [N, H]
+  size_t off_pcnt, off_ppos, off_prow, off_plab, off_pgrow, off_ph;
   size_t total;
 };
+
+// Rows per block of the valid-row packing scan.
+constexpr int64_t kPackRows = 1024;
 
 // Returns FLCE_OK and fills `out`, or an error code (no plan fits the budget).
 int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, bool fwd_only, Plan* out);

@@ -12,9 +12,17 @@
 //   grad_h_reduce  grad_h rows = sum of the slices, cast to the storage dtype
 //   grad_W         grad_W (+)= G^T h_c (MFMA), fp32, overwrite on the first chunk
 //                  unless the caller accumulates
-// and once per call: header_init, label_scan (before), finalize (after).  The
-// forward-only entry runs fwd_logits (without storing z) and row_merge per
-// chunk, then finalize.
+// and once per call: header_init, the label scan with valid-row packing
+// (before), finalize (after).  The forward-only entry runs fwd_logits (without
+// storing z) and row_merge per chunk, then finalize.
+//
+// Valid-row packing: ignored rows add nothing to the loss or to either
+// gradient, so unless every row's log-sum-exp or argmax is requested the
+// valid rows of h are first gathered, in order, into a packed copy, and the
+// chunks run over packed rows: the GEMMs skip whole token tiles and K steps
+// past N_valid.  N_valid is known only on the device; the host plans for N
+// rows and each kernel reads its chunk's row count (chunk_rows), so nothing
+// synchronises.
 #include "kernel_args.hpp"
 #include "gemm_tile.hpp"
 #include "common_kernels.hpp"
@@ -35,7 +43,7 @@ namespace flce {
 constexpr int kZStage = 4096;   // LDS byte offset of the z staging buffers (after the row partials)
 
 template <typename T, bool kCap, bool kStoreZ>
-__device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn,
+__device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs& p, int tm, int tn, int Ct,
                                              char* smem) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
@@ -59,7 +67,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
         }
     }
     const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
-    const bool tok_ok = tok < p.C_this;
+    const bool tok_ok = tok < Ct;
     const int64_t lab64 = tok_ok ? p.labels[tok] : -1;
     // first maximum: one chain per bm, columns ascending inside each
     float mxb[4];
@@ -123,7 +131,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
         const int r = 4 * k + (lane >> 4);
         const u32x4 w = *reinterpret_cast<const u32x4*>(zs + r * 256 + ((u ^ (r & 15)) << 4));
         const int t = tn * kTile + wn * 128 + bn * 32 + r;
-        if (t < p.C_this) *reinterpret_cast<u32x4*>(zcol + (int64_t)t * p.ldz) = w;
+        if (t < Ct) *reinterpret_cast<u32x4*>(zcol + (int64_t)t * p.ldz) = w;
       }
     } else if (kStoreZ && tok_ok) {
       T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + (int64_t)tok * p.ldz);
@@ -170,7 +178,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
     for (int bn = 0; bn < 4; ++bn) {
       const int idx = wn * 128 + bn * 32 + lo;
       const int tok = tn * kTile + idx;
-      if (tok < p.C_this) {
+      if (tok < Ct) {
         merge_stats(best[bn], sum[bn], bidx[bn], red_m[idx], red_s[idx], red_a[idx]);
         const int64_t o = (int64_t)tm * p.ldp + tok;
         p.pmax[o] = best[bn];
@@ -188,21 +196,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_logits_kernel(FwdArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
+  const int Ct = chunk_rows(p.packed, p.c0, p.C_this);
+  if (tn * kTile >= Ct) return;   // token tile past the chunk's (packed) rows
   const int64_t kbytes = (int64_t)p.H * Elem<T>::size;
   f32x16 acc[4][4];
   zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
-    gemm_kmajor_direct(p.W, p.ldw, tm * kTile, p.V, p.h, p.ldh, tn * kTile, p.C_this, kbytes, smem, acc);
+    gemm_kmajor_direct(p.W, p.ldw, tm * kTile, p.V, p.h, p.ldh, tn * kTile, Ct, kbytes, smem, acc);
   } else {
     KMajorLoader la, lb;
     la.init(p.W, p.ldw, tm * kTile, p.V, kbytes, 0);
-    lb.init(p.h, p.ldh, tn * kTile, p.C_this, kbytes, 0);
+    lb.init(p.h, p.ldh, tn * kTile, Ct, kbytes, 0);
     gemm_mainloop<T>(la, lb, (int)((kbytes + kKBytes - 1) / kKBytes), smem, acc);
   }
   if (p.T > 0.0f)
-    fwd_epilogue<T, true, kStoreZ>(acc, p, tm, tn, smem);
+    fwd_epilogue<T, true, kStoreZ>(acc, p, tm, tn, Ct, smem);
   else
-    fwd_epilogue<T, false, kStoreZ>(acc, p, tm, tn, smem);
+    fwd_epilogue<T, false, kStoreZ>(acc, p, tm, tn, Ct, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -214,9 +224,10 @@ __global__ __launch_bounds__(1024) void row_merge_kernel(MergeArgs p) {
   __shared__ int sa[16][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int tok = blockIdx.x * 64 + lane;
+  const int Ct = chunk_rows(p.packed, p.c0, p.C_this);
   float m = kNegInf, s = 0.0f;
   int a = 0x7fffffff;
-  if (tok < p.C_this) {
+  if (tok < Ct) {
     for (int vt = w; vt < p.nvt; vt += 16) {
       const int64_t o = (int64_t)vt * p.ldp + tok;
       merge_stats(m, s, a, p.pmax[o], p.psum[o], p.parg[o]);
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(1024) void row_merge_kernel(MergeArgs p) {
   ss[w][lane] = s;
   sa[w][lane] = a;
   __syncthreads();
-  if (w == 0 && tok < p.C_this) {
+  if (w == 0 && tok < Ct) {
     for (int k = 1; k < 16; ++k) merge_stats(m, s, a, sm[k][lane], ss[k][lane], sa[k][lane]);
     const float l = m + logf(s);
     const int64_t lab = p.labels[tok];
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256) void grad_logits_kernel(GradLogitArgs p) {
   constexpr int E = Elem<T>::per_chunk;
   const int64_t vecs = p.Vp / E;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= vecs * p.C_this) return;
+  if (idx >= vecs * chunk_rows(p.packed, p.c0, p.C_this)) return;
   const int64_t row = idx / vecs;
   const int col0 = (int)(idx - row * vecs) * E;
   T* zr = reinterpret_cast<T*>(static_cast<char*>(p.z) + row * p.ldz) + col0;
@@ -285,6 +296,8 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
   int tm, tn, sp;
   map_tile(p.map, tm, tn, sp);
+  const int Ct = chunk_rows(p.packed, p.c0, p.C_this);
+  if (tm * kTile >= Ct) return;   // token tile past the chunk's (packed) rows
   const int k0 = sp * p.ksteps_per_split;
   const int rem = p.ksteps_total - k0;
   const int nk = rem < p.ksteps_per_split ? rem : p.ksteps_per_split;
@@ -295,13 +308,13 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
     static_assert(kKBytes == kDKBytes, "one K step per planned step");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     KMajorDirect<false> la;   // rows of Vp elements: whole K steps
-    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * 2, k0, (wave >> 1) * 128, lane);
+    la.init(p.G, p.ldg, tm * kTile, Ct, (int64_t)p.Vp * 2, k0, (wave >> 1) * 128, lane);
     MNMajorDirect lb;
     lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0, (wave & 1) * 128, lane);
     gemm_mainloop_direct(la, lb, nk, smem, acc);
   } else {
     KMajorLoader la;
-    la.init(p.G, p.ldg, tm * kTile, p.C_this, (int64_t)p.Vp * Elem<T>::size, k0);
+    la.init(p.G, p.ldg, tm * kTile, Ct, (int64_t)p.Vp * Elem<T>::size, k0);
     MNMajorLoader<T> lb;
     lb.init(p.W, p.ldw, tn * kTile, p.H, p.V, k0);
     gemm_mainloop<T>(la, lb, nk, smem, acc);
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
 // grad_h rows = sum of the split partials, in split order.  One thread per
 // lane group of a tile: its 16 values sit in 4 quads 1 KB apart (the layout
 // grad_h_kernel stores) and map to rows 8 (v >> 2) + 4 hi + (v & 3) of a
-// 32 x 32 block at column lo.
+// 32 x 32 block at column lo.  Packed rows go back to the caller's rows.
 template <typename T>
 __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -334,6 +347,8 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
   const int lane = r & 63, blk = r >> 6;           // blk = (wave * 4 + bm) * 4 + bn
   const int wave = blk >> 4, bm = (blk >> 2) & 3, bn = blk & 3;
   const int tm = tile / p.tiles_n, tn = tile - tm * p.tiles_n;
+  const int Ct = chunk_rows(p.packed, p.c0, p.C_this);
+  if (tm * kTile >= Ct) return;   // no partials were written for this tile
   const int col = tn * kTile + (wave & 1) * 128 + bn * 32 + (lane & 31);
   const int row0 = tm * kTile + (wave >> 1) * 128 + bm * 32 + 4 * (lane >> 5);
   const float* src = p.part + ((int64_t)tile << 16) + blk * 1024 + lane * 4;
@@ -350,7 +365,10 @@ __global__ __launch_bounds__(256) void grad_h_reduce_kernel(GradHReduceArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = row0 + 8 * j + e;
-      if (row < p.C_this) out[(int64_t)row * p.H + col] = (T)a[j][e];
+      if (row < Ct) {
+        const int64_t orow = p.prow ? (int64_t)p.prow[p.c0 + row] : p.c0 + row;
+        out[orow * p.H + col] = (T)a[j][e];
+      }
     }
 }
 
@@ -419,24 +437,152 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
   map_tile(p.map, tm, tn, sp);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
+  // K = the chunk's (packed) rows; an empty chunk adds nothing, and the first
+  // chunk with no rows still overwrites grad_W with zeros
+  const int Ct = chunk_rows(p.packed, p.c0, p.C_this);
+  if (kAccumulate && Ct == 0) return;
   f32x16 acc[4][4];
   zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
     MNMajorDirect la, lb;
-    la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0, wm * 128, lane);
-    lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0, wn * 128, lane);
+    la.init(p.h, p.ldh, tm * kTile, p.H, Ct, 0, wm * 128, lane);
+    lb.init(p.G, p.ldg, tn * kTile, p.Vp, Ct, 0, wn * 128, lane);
     constexpr int bk = kDKBytes / 2;
-    gemm_mainloop_direct(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
+    gemm_mainloop_direct(la, lb, (Ct + bk - 1) / bk, smem, acc);
   } else {
     MNMajorLoader<T> la, lb;
-    la.init(p.h, p.ldh, tm * kTile, p.H, p.C_this, 0);
-    lb.init(p.G, p.ldg, tn * kTile, p.Vp, p.C_this, 0);
+    la.init(p.h, p.ldh, tm * kTile, p.H, Ct, 0);
+    lb.init(p.G, p.ldg, tn * kTile, p.Vp, Ct, 0);
     constexpr int bk = kKBytes / Elem<T>::size;
-    gemm_mainloop<T>(la, lb, (p.C_this + bk - 1) / bk, smem, acc);
+    gemm_mainloop<T>(la, lb, (Ct + bk - 1) / bk, smem, acc);
   }
   // the K loop ended with a barrier: the LDS is free, 32 KB per wave
   store_grad_W_rows<kAccumulate>(acc, p.gW, p.H, p.V, tn * kTile + wn * 128, tm * kTile + wm * 128,
                                  smem + wave * 32768);
+}
+
+// ---------------------------------------------------------------------------
+// Valid-row packing (before the first chunk; no host synchronisation).
+//   pack_count    per block of kPackRows rows: the valid count, plus N_valid
+//                 and the label range check of the label scan
+//   pack_offsets  exclusive prefix sum of the block counts (one block)
+//   pack_rows     each row's packed position (-1: ignored); for each packed
+//                 row its original row, label and upstream row gradient
+//   pack_gather   h rows into the packed copy; grad_h rows of ignored rows
+//                 are zeroed here (no chunk writes them)
+static_assert(kPackRows == 4 * 256, "four rows per thread");
+
+__global__ __launch_bounds__(256) void pack_count_kernel(const int64_t* labels, int64_t N, int64_t V,
+                                                         int64_t ignore_index, Header* hdr, int* cnt) {
+  __shared__ int sc[256];
+  __shared__ int sb[256];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kPackRows + 4 * t;
+  int c = 0, b = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (r0 + k < N) {
+      const int64_t l = labels[r0 + k];
+      if (l != ignore_index) {
+        ++c;
+        if (l < 0 || l >= V) b = 1;
+      }
+    }
+  }
+  sc[t] = c;
+  sb[t] = b;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+      sc[t] += sc[t + w];
+      sb[t] |= sb[t + w];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    cnt[blockIdx.x] = sc[0];
+    if (sc[0]) atomicAdd(&hdr->n_valid, (unsigned long long)sc[0]);
+    if (sb[0]) atomicOr(&hdr->status, FLCE_ELABEL);
+  }
+}
+
+// In place: cnt[b] becomes the number of valid rows before block b.
+__global__ __launch_bounds__(1024) void pack_offsets_kernel(int* cnt, int64_t nb) {
+  __shared__ int s[1024];
+  const int t = threadIdx.x;
+  int carry = 0;
+  for (int64_t base = 0; base < nb; base += 1024) {
+    const int64_t i = base + t;
+    const int v = i < nb ? cnt[i] : 0;
+    s[t] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {   // inclusive scan
+      const int x = t >= off ? s[t - off] : 0;
+      __syncthreads();
+      s[t] += x;
+      __syncthreads();
+    }
+    if (i < nb) cnt[i] = carry + s[t] - v;
+    carry += s[1023];
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_rows_kernel(const int64_t* labels, int64_t N, int64_t ignore_index,
+                                                        const int* boff, const float* grad_rows, int* ppos,
+                                                        int* prow, int64_t* plab, float* pgrow) {
+  __shared__ int s[256];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kPackRows + 4 * t;
+  int64_t lab[4];
+  bool ok[4];
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    lab[k] = r0 + k < N ? labels[r0 + k] : ignore_index;
+    ok[k] = r0 + k < N && lab[k] != ignore_index;
+    c += ok[k] ? 1 : 0;
+  }
+  s[t] = c;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {   // inclusive scan
+    const int x = t >= off ? s[t - off] : 0;
+    __syncthreads();
+    s[t] += x;
+    __syncthreads();
+  }
+  int pos = boff[blockIdx.x] + s[t] - c;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t i = r0 + k;
+    if (i >= N) break;
+    if (ok[k]) {
+      ppos[i] = pos;
+      prow[pos] = (int)i;
+      plab[pos] = lab[k];
+      if (grad_rows) pgrow[pos] = grad_rows[i];
+      ++pos;
+    } else {
+      ppos[i] = -1;
+    }
+  }
+}
+
+// One row per block pass, 16 bytes per thread; row_bytes is a multiple of 16.
+__global__ __launch_bounds__(256) void pack_gather_kernel(const char* h, int64_t N, int64_t row_bytes,
+                                                          const int* ppos, char* ph, char* grad_h) {
+  const int64_t nvec = row_bytes / 16;
+  for (int64_t i = blockIdx.x; i < N; i += gridDim.x) {
+    const int q = ppos[i];
+    if (q >= 0) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(h + i * row_bytes);
+      u32x4* dst = reinterpret_cast<u32x4*>(ph + (int64_t)q * row_bytes);
+      for (int64_t e = threadIdx.x; e < nvec; e += 256) dst[e] = src[e];
+    } else if (grad_h) {
+      u32x4* dst = reinterpret_cast<u32x4*>(grad_h + i * row_bytes);
+      for (int64_t e = threadIdx.x; e < nvec; e += 256) dst[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -459,6 +605,15 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   int* parg = reinterpret_cast<int*>(ws + pl.off_parg);
   void* zbuf = ws + pl.off_z;
   float* ghpart = reinterpret_cast<float*>(ws + pl.off_ghpart);
+  int* pcnt = reinterpret_cast<int*>(ws + pl.off_pcnt);
+  int* ppos = reinterpret_cast<int*>(ws + pl.off_ppos);
+  int* prow = reinterpret_cast<int*>(ws + pl.off_prow);
+  int64_t* plab = reinterpret_cast<int64_t*>(ws + pl.off_plab);
+  float* pgrow = reinterpret_cast<float*>(ws + pl.off_pgrow);
+  char* ph = ws + pl.off_ph;
+  // every row's log-sum-exp and argmax are outputs only without packing
+  const bool pack = a.N > 0 && !a.lse_rows && !a.pred_rows;
+  const Header* packed = pack ? hdr : nullptr;
 
   const int H = (int)a.H, V = (int)a.V, Vp = (int)pl.Vp;
   const int C = (int)pl.C;
@@ -468,7 +623,16 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   {
     ProfileScope ps(FLCE_KERNEL_LABEL_SCAN, st);
     header_init_kernel<<<1, 64, 0, st>>>(hdr);
-    if (a.N > 0) {
+    if (pack) {
+      const int64_t nb = (a.N + kPackRows - 1) / kPackRows;
+      pack_count_kernel<<<(unsigned)nb, 256, 0, st>>>(a.labels, a.N, a.V, a.ignore_index, hdr, pcnt);
+      pack_offsets_kernel<<<1, 1024, 0, st>>>(pcnt, nb);
+      pack_rows_kernel<<<(unsigned)nb, 256, 0, st>>>(a.labels, a.N, a.ignore_index, pcnt, a.grad_rows, ppos,
+                                                     prow, plab, pgrow);
+      const int64_t g = a.N < 16384 ? a.N : 16384;
+      pack_gather_kernel<<<(unsigned)g, 256, 0, st>>>(static_cast<const char*>(a.h), a.N, a.H * es, ppos, ph,
+                                                      a.fwd_only ? nullptr : static_cast<char*>(a.grad_h));
+    } else if (a.N > 0) {
       const unsigned g = grid_1d(a.N, 256);
       label_scan_kernel<<<g < 1024 ? g : 1024, 256, 0, st>>>(a.labels, a.N, a.V, a.ignore_index, hdr);
     }
@@ -482,8 +646,10 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   for (int64_t ck = 0; ck < pl.n_chunks; ++ck) {
     const int64_t c0 = ck * pl.C;
     const int Ct = (int)((a.N - c0) < pl.C ? (a.N - c0) : pl.C);
-    const char* hc = static_cast<const char*>(a.h) + c0 * a.H * es;
-    const int64_t* lc = a.labels + c0;
+    // unpacked: the caller's rows c0..; packed: packed rows c0.. (Ct is then
+    // an upper bound and the kernels read the chunk's rows on the device)
+    const char* hc = (pack ? ph : static_cast<const char*>(a.h)) + c0 * a.H * es;
+    const int64_t* lc = (pack ? plab : a.labels) + c0;
     const int tiles_tok = (Ct + kTile - 1) / kTile;
     const int tiles_voc = Vp / kTile;
     const int tiles_hid = (H + kTile - 1) / kTile;
@@ -497,6 +663,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     f.pmax = pmax; f.psum = psum; f.parg = parg; f.ldp = C;
     f.zlab = zlab + c0;
     f.map = TileMap{tiles_voc, tiles_tok, 1, 4, 1, 0};
+    f.packed = packed; f.c0 = c0;
     {
       ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
       if (a.fwd_only)
@@ -510,6 +677,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     m.labels = lc; m.ignore_index = a.ignore_index;
     m.zlab = zlab + c0; m.lse = lse + c0; m.loss_row = loss_row + c0; m.pred = pred + c0;
     m.C_this = Ct;
+    m.packed = packed; m.c0 = c0;
     {
       ProfileScope ps(FLCE_KERNEL_ROW_MERGE, st);
       row_merge_kernel<<<grid_1d(Ct, 64), 1024, 0, st>>>(m);
@@ -520,7 +688,9 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gl.z = zbuf; gl.ldz = (int64_t)Vp * es; gl.C_this = Ct; gl.V = V; gl.Vp = Vp;
     gl.labels = lc; gl.ignore_index = a.ignore_index; gl.lse = lse + c0; gl.hdr = hdr;
     gl.reduction = a.reduction; gl.mult = a.multiplier; gl.T = capT; gl.invT = invT;
-    gl.grad_scale = a.grad_scale; gl.grad_rows = a.grad_rows ? a.grad_rows + c0 : nullptr;
+    gl.grad_scale = a.grad_scale;
+    gl.grad_rows = a.grad_rows ? (pack ? pgrow : a.grad_rows) + c0 : nullptr;
+    gl.packed = packed; gl.c0 = c0;
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_LOGITS, st);
       grad_logits_kernel<T><<<grid_1d((int64_t)Ct * (Vp / Elem<T>::per_chunk), 256), 256, 0, st>>>(gl);
@@ -535,6 +705,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     const int64_t part_stride = ((int64_t)((C + kTile - 1) / kTile) * tiles_hid) << 16;
     gh.part = ghpart; gh.part_stride = part_stride;
     gh.map = TileMap{tiles_tok, tiles_hid, splits, tiles_tok, 0, 0};
+    gh.packed = packed; gh.c0 = c0;
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_H, st);
       grad_h_kernel<T><<<tiles_tok * tiles_hid * splits, kThreads, 0, st>>>(gh);
@@ -544,7 +715,8 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gr.part = ghpart; gr.part_stride = part_stride; gr.splits = splits;
     gr.C_this = Ct; gr.H = H; gr.tiles_n = tiles_hid;
     gr.groups = (int64_t)tiles_tok * tiles_hid * 4096;
-    gr.out = static_cast<char*>(a.grad_h) + c0 * a.H * es;
+    gr.out = a.grad_h;
+    gr.packed = packed; gr.c0 = c0; gr.prow = pack ? prow : nullptr;
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_H_REDUCE, st);
       grad_h_reduce_kernel<T><<<grid_1d(gr.groups, 256), 256, 0, st>>>(gr);
@@ -555,6 +727,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gw.C_this = Ct; gw.H = H; gw.V = V; gw.Vp = Vp;
     gw.gW = a.grad_W; gw.accumulate = (ck > 0 || a.accumulate_grad_W) ? 1 : 0;
     gw.map = TileMap{tiles_hid, tiles_voc, 1, 4, 1, 1};
+    gw.packed = packed; gw.c0 = c0;
     {
       ProfileScope ps(FLCE_KERNEL_GRAD_W, st);
       if (gw.accumulate)
@@ -568,6 +741,10 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   fa.loss_row = loss_row; fa.lse = lse; fa.pred = pred; fa.hdr = hdr; fa.reduction = a.reduction;
   fa.loss = a.loss; fa.n_correct = a.n_correct;
   fa.loss_rows = a.loss_rows; fa.lse_rows = a.lse_rows; fa.pred_rows = a.pred_rows;
+  if (pack) {
+    fa.ppos = ppos;
+    fa.plab = plab;
+  }
   {
     ProfileScope ps(FLCE_KERNEL_FINALIZE, st);
     finalize_kernel<<<1, 1024, 0, st>>>(fa);

@@ -11,6 +11,10 @@
 // The forward-only plan stores no logits at all (only 12 bytes of partials
 // per token and 256-vocabulary tile), so its chunk is as large as the budget
 // allows, up to all N rows.
+//
+// Both plans also hold a packed copy of the valid (non-ignored) rows of h
+// with their labels: ignored rows add nothing to the loss or the gradients,
+// so the GEMMs can run over the valid rows alone, chunked in packed order.
 #include <algorithm>
 
 #include "flce_internal.hpp"
@@ -73,6 +77,14 @@ void layout(Plan* p) {
     const size_t tiles = size_t((p->C + kRowTile - 1) / kRowTile) * size_t((p->H + 255) / 256);
     p->off_ghpart = take(size_t(p->split_k) * tiles * 65536 * 4);
   }
+  // valid-row packing (used unless every row's log-sum-exp or argmax is
+  // requested): the GEMMs then run over the non-ignored rows only
+  p->off_pcnt = take(size_t((p->N + kPackRows - 1) / kPackRows) * 4);
+  p->off_ppos = take(N * 4);
+  p->off_prow = take(N * 4);
+  p->off_plab = take(N * 8);
+  p->off_pgrow = take(N * 4);
+  p->off_ph = take(N * size_t(p->H) * size_t(p->es));
   p->total = off;
 }
 

@@ -7,6 +7,16 @@
 
 namespace flce {
 
+// Rows of the current chunk.  `rows` is the host's count; with valid-row
+// packing (`packed` = the header) the chunk starts at packed row c0 and holds
+// the valid rows left from there, at most `rows`: N_valid is known only on
+// the device, so every kernel of the chunk reads it there.
+__device__ __forceinline__ int chunk_rows(const Header* packed, int64_t c0, int rows) {
+  if (!packed) return rows;
+  const int64_t left = (int64_t)packed->n_valid - c0;
+  return left <= 0 ? 0 : (left < rows ? (int)left : rows);
+}
+
 struct FwdArgs {
   const void* h;
   const void* W;
@@ -22,6 +32,8 @@ struct FwdArgs {
   int ldp;
   float* zlab;
   TileMap map;
+  const Header* packed = nullptr;   // valid-row packing: chunk rows from N_valid (null: C_this)
+  int64_t c0 = 0;                   // first (packed) row of the chunk
 };
 
 struct MergeArgs {
@@ -36,6 +48,8 @@ struct MergeArgs {
   float* loss_row;
   int* pred;
   int C_this;
+  const Header* packed = nullptr;   // valid-row packing: chunk rows from N_valid (null: C_this)
+  int64_t c0 = 0;                   // first (packed) row of the chunk
 };
 
 struct GradLogitArgs {
@@ -50,6 +64,8 @@ struct GradLogitArgs {
   float mult, T, invT;
   float grad_scale;         // upstream gradient of the scalar loss
   const float* grad_rows;   // per-row upstream gradients (reduction none) or null
+  const Header* packed = nullptr;   // valid-row packing: chunk rows from N_valid (null: C_this)
+  int64_t c0 = 0;                   // first (packed) row of the chunk
 };
 
 struct GradHArgs {
@@ -62,6 +78,8 @@ struct GradHArgs {
   float* part;
   int64_t part_stride;
   TileMap map;
+  const Header* packed = nullptr;   // valid-row packing: chunk rows from N_valid (null: C_this)
+  int64_t c0 = 0;                   // first (packed) row of the chunk
 };
 
 struct GradHReduceArgs {
@@ -71,6 +89,9 @@ struct GradHReduceArgs {
   int C_this, H, tiles_n;
   int64_t groups;   // 16-value lane groups: 4096 per 256 x 256 tile
   void* out;
+  const Header* packed = nullptr;
+  int64_t c0 = 0;
+  const int* prow = nullptr;   // packed: original row of each packed row (null: rows c0 + r of out)
 };
 
 struct GradWArgs {
@@ -82,6 +103,8 @@ struct GradWArgs {
   float* gW;
   int accumulate;
   TileMap map;
+  const Header* packed = nullptr;   // valid-row packing: chunk rows from N_valid (null: C_this)
+  int64_t c0 = 0;                   // first (packed) row of the chunk
 };
 
 struct FinalizeArgs {
@@ -97,6 +120,11 @@ struct FinalizeArgs {
   float* loss_rows;     // optional per-row outputs (null: skipped)
   float* lse_rows;
   int64_t* pred_rows;
+  // valid-row packing (null: unpacked): loss_row / pred hold the N_valid
+  // packed rows, ppos maps each row to its packed row (-1: ignored), plab
+  // holds the packed labels
+  const int* ppos = nullptr;
+  const int64_t* plab = nullptr;
 };
 
 }  // namespace flce

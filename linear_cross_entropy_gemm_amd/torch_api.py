@@ -56,11 +56,14 @@ def _prepare(h, W, labels, reduction):
     return h2, W.contiguous(), lab
 
 
-def _row_buffers(N: int, dev, want: bool):
-    if not want:
-        return None, None, None
-    return (torch.empty(N, dtype=torch.float32, device=dev), torch.empty(N, dtype=torch.float32, device=dev),
-            torch.empty(N, dtype=torch.int64, device=dev))
+def _row_buffers(N: int, dev, want_loss: bool, want_stats: bool):
+    """Per-row loss (reduction "none" or row_outputs) and per-row log-sum-exp /
+    argmax (row_outputs only: asking for them keeps the ignored rows in the
+    GEMMs, since those two are defined for every row)."""
+    loss_rows = torch.empty(N, dtype=torch.float32, device=dev) if want_loss or want_stats else None
+    if not want_stats:
+        return loss_rows, None, None
+    return loss_rows, torch.empty(N, dtype=torch.float32, device=dev), torch.empty(N, dtype=torch.int64, device=dev)
 
 
 def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
@@ -99,7 +102,7 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
         )
     want_rows = row_outputs or reduction == "none"
     if want_rows and out.loss_rows is None:
-        out.loss_rows, out.lse_rows, out.pred_rows = _row_buffers(N, dev, True)
+        out.loss_rows, out.lse_rows, out.pred_rows = _row_buffers(N, dev, True, row_outputs)
     gr = None
     if grad_rows is not None:
         gr = grad_rows.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
@@ -107,8 +110,8 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
             raise ValueError("grad_rows must have one entry per row")
     opts = _lib.flce_options_t(
         loss_rows=_ptr(out.loss_rows) if want_rows else None,
-        lse_rows=_ptr(out.lse_rows) if want_rows else None,
-        pred_rows=_ptr(out.pred_rows) if want_rows else None,
+        lse_rows=_ptr(out.lse_rows) if row_outputs else None,
+        pred_rows=_ptr(out.pred_rows) if row_outputs else None,
         grad_rows=_ptr(gr), grad_scale=float(grad_scale), accumulate_grad_W=1 if accumulate_grad_W else 0)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = _lib.flce_fwd_bwd_ex(_ptr(h2), _ptr(Wc), _ptr(lab), N, H, V, int(ignore_index),
@@ -142,8 +145,7 @@ def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     dev = h.device
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    want_rows = row_outputs or reduction == "none"
-    loss_rows, lse_rows, pred_rows = _row_buffers(N, dev, want_rows)
+    loss_rows, lse_rows, pred_rows = _row_buffers(N, dev, reduction == "none", row_outputs)
     res = FlceForward(loss=torch.empty((), dtype=torch.float32, device=dev),
                       n_correct=torch.empty((), dtype=torch.int64, device=dev), workspace=workspace,
                       loss_rows=loss_rows, lse_rows=lse_rows, pred_rows=pred_rows)
@@ -225,7 +227,7 @@ def cross_entropy(z: torch.Tensor, labels: torch.Tensor, ignore_index: int = -10
         g = z if in_place else torch.empty((N, z.stride(0)), dtype=z.dtype, device=dev)
         res.grad_logits = g if in_place else g[:, :V]
     want_rows = row_outputs or reduction == "none"
-    res.loss_rows, res.lse_rows, res.pred_rows = _row_buffers(N, dev, want_rows)
+    res.loss_rows, res.lse_rows, res.pred_rows = _row_buffers(N, dev, want_rows, want_rows)
     gr = None
     if grad_rows is not None:
         gr = grad_rows.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()

@@ -220,11 +220,16 @@ def test_forward_only_plan_is_smaller_and_unchunked():
         fb = L.flce_workspace_size(N, H, V, dt)
         fo = L.flce_fwd_workspace_size(N, H, V, dt)
         assert 0 < fo < fb
-        # one chunk of all N rows: header + 4 row arrays + 3 partial arrays of [V/256, N]
+        # one chunk of all N rows: header + 4 row arrays + 3 partial arrays of [V/256, N],
+        # plus the packed valid rows: position, row, label, row gradient and the h copy
         nvt = (V + 255) // 256
-        assert fo >= 256 + 4 * 4 * N + 3 * 4 * nvt * N
-    # no logits transient: the c4 forward workspace stays under 0.1 GB
-    assert L.flce_fwd_workspace_size(8192, 6656, 202048, 0) < 1e8
+        es = 2 if dt == 0 else 4
+        assert fo >= 256 + 4 * 4 * N + 3 * 4 * nvt * N + (4 + 4 + 8 + 4) * N + N * H * es
+        # the full call holds the same packed rows on top of its logits transient
+        assert fb >= fo + ((N + 1) // 2) * nvt * 256 * es - 3 * 4 * nvt * N
+    # no logits transient: the c4 forward workspace is the 109 MB packed copy of h
+    # plus 78 MB of row arrays and partials, under 0.2 GB
+    assert L.flce_fwd_workspace_size(8192, 6656, 202048, 0) < 2e8
     assert L.flce_fwd_workspace_size(4, 12, 8, 0) == 0          # unsupported H
 
 

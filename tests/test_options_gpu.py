@@ -84,6 +84,15 @@ def test_forward_only(cid, base, N, H, V, T, m, red):
     assert torch.equal(f.loss_rows, o.loss_rows)
     assert torch.equal(f.lse_rows, o.lse_rows)
     assert torch.equal(f.pred_rows, o.pred_rows)
+    # without every row's lse / argmax the ignored rows are packed out: the
+    # same per-row statistics, summed over the packed rows
+    fp = L.forward(h, W, lab, IGN, softcap(case), m, red)
+    op = L.fwd_bwd(h, W, lab, IGN, softcap(case), m, red)
+    torch.cuda.synchronize()
+    assert fp.lse_rows is None and fp.pred_rows is None
+    assert fp.loss.item() == op.loss.item()
+    assert int(fp.n_correct.item()) == int(f.n_correct.item()) == int(op.n_correct.item())
+    assert abs(fp.loss.item() - loss) <= 1e-6 * abs(loss)
 
 
 @pytest.mark.parametrize("cid,base,N,H,V,T,m,red", SHAPES[:3], ids=[s[0] for s in SHAPES[:3]])
@@ -95,19 +104,28 @@ def test_reduction_none_row_gradients(cid, base, N, H, V, T, m, red):
     h, W, lab = to_device(case)
     w = np.random.default_rng(77).normal(size=N).astype(np.float32)
     w[::7] = 0.0
-    o = L.fwd_bwd(h, W, lab, IGN, softcap(case), m, "none", grad_rows=torch.from_numpy(w).to(h.device))
-    torch.cuda.synchronize()
     ref = oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, IGN, T, m, "none",
                                 grad_rows=w.astype(np.float64))
     lt, gt = tolerances(case.cfg.dtype)
-    e_loss = abs(o.loss.item() - ref["loss"]) / abs(ref["loss"])
-    e_gh = rel_fro(o.grad_h.float().cpu().numpy(), ref["grad_h"])
-    e_gW = rel_fro(o.grad_W.cpu().numpy(), ref["grad_W"])
-    log(f"  sum of rows rel {e_loss:.2e} | grad_h {e_gh:.2e} grad_W {e_gW:.2e}")
-    assert e_loss <= lt and e_gh <= gt and e_gW <= gt
-    check_rows(case, ref, o.loss_rows, o.lse_rows, o.pred_rows)
-    gh = o.grad_h.float().cpu().numpy()
-    assert np.all(gh[(case.labels == IGN) | (w == 0.0)] == 0.0)
+    # packed rows (row losses only) and all rows (with every row's lse / argmax)
+    for row_outputs in (False, True):
+        o = L.fwd_bwd(h, W, lab, IGN, softcap(case), m, "none", grad_rows=torch.from_numpy(w).to(h.device),
+                      row_outputs=row_outputs)
+        torch.cuda.synchronize()
+        e_loss = abs(o.loss.item() - ref["loss"]) / abs(ref["loss"])
+        e_gh = rel_fro(o.grad_h.float().cpu().numpy(), ref["grad_h"])
+        e_gW = rel_fro(o.grad_W.cpu().numpy(), ref["grad_W"])
+        log(f"  row_outputs={row_outputs}: sum of rows rel {e_loss:.2e} | grad_h {e_gh:.2e} grad_W {e_gW:.2e}")
+        assert e_loss <= lt and e_gh <= gt and e_gW <= gt
+        if row_outputs:
+            check_rows(case, ref, o.loss_rows, o.lse_rows, o.pred_rows)
+        else:
+            assert o.lse_rows is None and o.pred_rows is None
+            lr = o.loss_rows.cpu().numpy().astype(np.float64)
+            assert np.max(np.abs(lr - ref["loss_rows"]) / np.maximum(np.abs(ref["loss_rows"]), 1.0)) <= lt
+            assert np.all(lr[case.labels == IGN] == 0.0)
+        gh = o.grad_h.float().cpu().numpy()
+        assert np.all(gh[(case.labels == IGN) | (w == 0.0)] == 0.0)
 
 
 def test_grad_scale_and_accumulate():

@@ -84,6 +84,39 @@ def test_parity_small(cid, base, N, H, V, T, m, red):
     check(case, o, ref)
 
 
+# (id, base, N, H, V, T, m, reduction, ignored fraction)
+PACK_CASES = [
+    ("bf16_tail_runs", "c5", 2600, 128, 700, 30.0, 1.0, "sum", 0.5),    # 325-row runs: whole tiles
+    ("bf16_mostly_ignored", "c2", 600, 96, 530, 1.0, 0.5, "mean", 0.6),  # later chunks empty
+    ("f32_half_ignored", "c1", 520, 64, 300, 2.0, 1.0, "mean", 0.5),
+]
+
+
+@pytest.mark.parametrize("cid,base,N,H,V,T,m,red,frac", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_packed_rows_match_all_rows(cid, base, N, H, V, T, m, red, frac):
+    """The default call packs the valid rows before the GEMMs; asking for
+    every row's lse / argmax runs all rows.  Both match the oracle, every
+    grad_h row is bitwise the same (the same per-row arithmetic, only the
+    row's place in the tiles differs) and n_correct is equal."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make(base, N, H, V, T, m, red, ignore_frac=frac)
+    c = case.cfg
+    log(f"[packing] {cid}: {c.dtype} N={c.N} H={c.H} V={c.V} valid={int((case.labels != IGN).sum())}")
+    ref = reference(case)
+    h, W, lab = to_device(case)
+    cap = c.softcap_T if c.softcap_T > 0 else None
+    packed = L.fwd_bwd(h, W, lab, IGN, cap, c.multiplier, c.reduction)
+    allrows = L.fwd_bwd(h, W, lab, IGN, cap, c.multiplier, c.reduction, row_outputs=True)
+    torch.cuda.synchronize()
+    check(case, packed, ref)
+    check(case, allrows, ref)
+    assert torch.equal(packed.grad_h, allrows.grad_h)
+    assert int(packed.n_correct.item()) == int(allrows.n_correct.item())
+    lp, la = float(packed.loss.item()), float(allrows.loss.item())
+    assert abs(lp - la) <= 1e-6 * abs(la)
+
+
 @pytest.mark.parametrize("dtype_base", ["c2", "c1"])
 def test_planted_labels_count_exactly(dtype_base):
     """Half of the valid rows get their own argmax as label, so n_correct is
