@@ -89,6 +89,7 @@ PACK_CASES = [
     ("bf16_tail_runs", "c5", 2600, 128, 700, 30.0, 1.0, "sum", 0.5),    # 325-row runs: whole tiles
     ("bf16_mostly_ignored", "c2", 600, 96, 530, 1.0, 0.5, "mean", 0.6),  # later chunks empty
     ("f32_half_ignored", "c1", 520, 64, 300, 2.0, 1.0, "mean", 0.5),
+    ("bf16_none_ignored", "c2", 1500, 64, 400, 0.0, 1.0, "mean", 0.0),   # N_valid = N, 2 pack blocks
 ]
 
 
