@@ -88,6 +88,33 @@ __device__ __forceinline__ void softcap_block(f32x16 (&acc)[4][4], int bn, float
   }
 }
 
+// The same on one token block already copied out of the accumulators
+// (x[bm] = acc[bm][bn]).
+template <bool kCap>
+__device__ __forceinline__ void softcap_cols(f32x16 (&x)[4], float scale, float T) {
+  bool need = false;
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      x[bm][v] *= scale;
+      if (kCap) need |= __builtin_fabsf(x[bm][v]) >= kTanhSeriesMax;
+    }
+  if (kCap) {
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[bm][v] = T * softcap_tanh(x[bm][v]);
+    } else {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[bm][v] = T * tanh_series(x[bm][v]);
+    }
+  }
+}
+
 // Online log-sum-exp / argmax state merge (running max m, sum of exp(z - m),
 // index of the first maximum).  Equal maxima keep the lower index.  An empty
 // state is (-inf, 0, INT_MAX); the merge is branch-free and never forms

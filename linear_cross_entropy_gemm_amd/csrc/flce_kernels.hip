@@ -52,10 +52,27 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
   const float scale = kCap ? p.mult * p.invT : p.mult;
   float best[4], sum[4];
   int bidx[4];
-  // One token block (bn) at a time, 64 values per lane.
-#pragma unroll
+  // One token block (bn) at a time, 64 values per lane, in a loop that is
+  // not unrolled: the block's accumulators are copied out first, so the
+  // epilogue's code exists once instead of four times (unrolled, it is several
+  // times the size of the instruction cache).
+#pragma unroll 1
   for (int bn = 0; bn < 4; ++bn) {
-    softcap_block<kCap>(acc, bn, scale, p.T);
+    f32x16 x[4];
+    if (bn == 0) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) x[bm] = acc[bm][0];
+    } else if (bn == 1) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) x[bm] = acc[bm][1];
+    } else if (bn == 2) {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) x[bm] = acc[bm][2];
+    } else {
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) x[bm] = acc[bm][3];
+    }
+    softcap_cols<kCap>(x, scale, p.T);
     // padding columns take no part in the statistics (-inf; exp(-inf) = 0)
     if (partial) {
 #pragma unroll
@@ -63,7 +80,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int col = vbase + bm * 32 + 8 * (v >> 2) + (v & 3);
-          acc[bm][bn][v] = col < p.V ? acc[bm][bn][v] : kNegInf;
+          x[bm][v] = col < p.V ? x[bm][v] : kNegInf;
         }
     }
     const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
@@ -81,9 +98,9 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
     for (int v = 0; v < 16; ++v)
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) {
-        const float x = acc[bm][bn][v];
-        const bool gt = x > mxb[bm];
-        mxb[bm] = gt ? x : mxb[bm];
+        const float y = x[bm][v];
+        const bool gt = y > mxb[bm];
+        mxb[bm] = gt ? y : mxb[bm];
         axb[bm] = gt ? vbase + bm * 32 + 8 * (v >> 2) + (v & 3) : axb[bm];
       }
     float mx = mxb[0];
@@ -105,7 +122,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const bool is_lab = d == bm * 32 + 8 * (v >> 2) + (v & 3);
-          zl = is_lab ? acc[bm][bn][v] : zl;
+          zl = is_lab ? x[bm][v] : zl;
           found |= is_lab;
         }
       if (found && lab64 < p.V) p.zlab[tok] = zl;
@@ -121,8 +138,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int u = (4 * bm + i) ^ (lo & 15);
-          store4(reinterpret_cast<bf16*>(zs + lo * 256 + (u << 4) + 8 * hi), acc[bm][bn][4 * i],
-                 acc[bm][bn][4 * i + 1], acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]);
+          store4(reinterpret_cast<bf16*>(zs + lo * 256 + (u << 4) + 8 * hi), x[bm][4 * i],
+                 x[bm][4 * i + 1], x[bm][4 * i + 2], x[bm][4 * i + 3]);
         }
       const int u = lane & 15;
       char* zcol = static_cast<char*>(p.z) + (int64_t)(tm * kTile + wm * 128 + 8 * u) * 2;
@@ -139,8 +156,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
       for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          store4(zr + vbase + bm * 32 + 8 * i, acc[bm][bn][4 * i], acc[bm][bn][4 * i + 1],
-                 acc[bm][bn][4 * i + 2], acc[bm][bn][4 * i + 3]);
+          store4(zr + vbase + bm * 32 + 8 * i, x[bm][4 * i], x[bm][4 * i + 1],
+                 x[bm][4 * i + 2], x[bm][4 * i + 3]);
     }
     // sum of exp(z - max): one partial sum per bm
     const float mref = mx == kNegInf ? 0.0f : mx;
@@ -149,15 +166,18 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 #pragma unroll
     for (int v = 0; v < 16; ++v)
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) sb[bm] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[bm][bn][v], kLog2e, off));
+      for (int bm = 0; bm < 4; ++bm) sb[bm] += __builtin_amdgcn_exp2f(__builtin_fmaf(x[bm][v], kLog2e, off));
     float s = (sb[0] + sb[1]) + (sb[2] + sb[3]);
     const float m2 = __shfl_xor(mx, 32);
     const float s2 = __shfl_xor(s, 32);
     const int a2 = __shfl_xor(ax, 32);
     merge_stats(mx, s, ax, m2, s2, a2);  // lanes 0-31 carry the pair's result onwards
-    best[bn] = mx;
-    sum[bn] = s;
-    bidx[bn] = ax;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      best[k] = k == bn ? mx : best[k];
+      sum[k] = k == bn ? s : sum[k];
+      bidx[k] = k == bn ? ax : bidx[k];
+    }
   }
   float* red_m = reinterpret_cast<float*>(smem);
   float* red_s = red_m + 256;
