@@ -310,7 +310,8 @@ __global__ __launch_bounds__(256) void grad_logits_kernel(GradLogitArgs p) {
 // ---------------------------------------------------------------------------
 // grad_h partial over one vocabulary slice: rows = tokens (M), cols = hidden
 // (N), K = vocabulary.  A = G [C][Vp] (K contiguous), B = W [V][H] (N
-// contiguous, transposed through registers).
+// contiguous: bf16 read with transposing LDS reads, fp32 transposed through
+// registers).
 template <typename T>
 __global__ __launch_bounds__(kThreads, 1) void grad_h_kernel(GradHArgs p) {
   __shared__ __attribute__((aligned(16))) char smem[sizeof(T) == 2 ? kDLdsBytes : kLdsBytes];
@@ -407,15 +408,28 @@ template <bool kAccumulate>
 __device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], float* gW, int64_t H, int V,
                                                   int n_base, int m_base, char* lds) {
   const int lane = threadIdx.x & 63, lo = lane & 31, hi = lane >> 5;
+  // The wave's rows n_base .. n_base + 127 of grad_W as one buffer range
+  // (fewer rows at the end of the vocabulary, none past it): loads and stores
+  // of rows past V fall outside it (stores are dropped, loads read 0), and
+  // columns past H get an offset outside it, so nothing branches and the
+  // waits for the stored values can count exactly (with a branch per store,
+  // every store waited for all earlier ones).  128 rows of at most 2^21
+  // hidden values stay below 2^30 bytes.
+  int rows = V - n_base;
+  rows = rows < 0 ? 0 : (rows > 128 ? 128 : rows);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc_wave(reinterpret_cast<const char*>(gW + (int64_t)n_base * H), (int64_t)rows * H * 4);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    // H is a multiple of 4, so m < H keeps the whole vector inside the row
+    const int m = m_base + half * 64 + 4 * (lane & 15);
+    const uint32_t col_off = m < H ? (uint32_t)m * 4u : kOOB;
     f32x4 old[32];
     if constexpr (kAccumulate) {
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
-        const int n = n_base + 4 * k + (lane >> 4), m = m_base + half * 64 + 4 * (lane & 15);
-        old[k] = (n < V && m < H) ? *reinterpret_cast<const f32x4*>(gW + (int64_t)n * H + m)
-                                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t off = col_off == kOOB ? kOOB : (uint32_t)(4 * k + (lane >> 4)) * (uint32_t)H * 4u + col_off;
+        old[k] = __builtin_bit_cast(f32x4, load16(rs, off));
       }
     }
 #pragma unroll
@@ -435,9 +449,8 @@ __device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], flo
       const int row = 4 * k + (lane >> 4), u = lane & 15;
       f32x4 v = *reinterpret_cast<const f32x4*>(lds + row * 256 + ((u ^ (row & 15)) << 4));
       if constexpr (kAccumulate) v += old[k];
-      const int n = n_base + row, m = m_base + half * 64 + 4 * u;
-      // H is a multiple of 4, so m < H keeps the whole vector inside the row
-      if (n < V && m < H) *reinterpret_cast<f32x4*>(gW + (int64_t)n * H + m) = v;
+      const uint32_t off = col_off == kOOB ? kOOB : (uint32_t)row * (uint32_t)H * 4u + col_off;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)off, 0, 0);
     }
   }
 }
@@ -445,7 +458,8 @@ __device__ __forceinline__ void store_grad_W_rows(const f32x16 (&acc)[4][4], flo
 // ---------------------------------------------------------------------------
 // grad_W (+)= G^T h_c, computed as its transpose h_c^T G: rows = hidden (M),
 // cols = vocabulary (N), K = tokens.  Both operands are stored with K as the
-// slow dimension and are transposed through registers.  With hidden on the M
+// slow dimension (bf16: transposing LDS reads; fp32: transposed through
+// registers).  With hidden on the M
 // side each lane owns 4 consecutive hidden entries of one vocabulary row of
 // grad_W per accumulator group, so the fp32 epilogue moves 16 bytes per
 // access.  For every chunk after the first (kAccumulate) the epilogue adds

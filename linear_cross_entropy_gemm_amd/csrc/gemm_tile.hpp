@@ -4,13 +4,18 @@
 // A work-group of 256 threads (4 waves of 64) owns a 256 x 256 output tile;
 // each wave owns a 128 x 128 quadrant computed as 4 x 4 blocks of the
 // 32 x 32 MFMA (bf16: v_mfma_f32_32x32x16_bf16, fp32: v_mfma_f32_32x32x2_f32).
-// Operand tiles are staged in LDS, double buffered (2 stages x (A + B) x
-// 32 KiB = 128 KiB of the 160 KiB per CU), always with K contiguous per row:
-// one K step is 128 bytes of K per row (64 bf16 or 32 fp32), i.e. 8 chunks of
-// 16 bytes.  Chunk c of row r sits at chunk slot c ^ ((r ^ (r >> 3)) & 7), so
-// that both the fragment reads (8 consecutive rows, same chunk) and the
-// transposing stores (rows 8 apart, same chunk) hit 8 distinct 16-byte bank
-// groups.
+// One K step is 128 bytes of K per operand row (64 bf16 or 32 fp32).
+//
+// bf16 (every lm_head shape): the direct-to-LDS pipeline further below, a
+// ring of five 32 KB operand slots (160 KB) filled by buffer loads that write
+// LDS directly; MN-major operands are read back with transposing LDS reads.
+//
+// fp32 (the small parity workload): the register-staged pipeline that comes
+// first, double buffered (2 stages x (A + B) x 32 KiB = 128 KiB), always with
+// K contiguous per row in LDS: 8 chunks of 16 bytes per row, chunk c of row r
+// at chunk slot c ^ ((r ^ (r >> 3)) & 7), so that both the fragment reads (8
+// consecutive rows, same chunk) and the transposing stores (rows 8 apart,
+// same chunk) hit 8 distinct 16-byte bank groups.
 //
 // MFMA operand layout: for the 32x32 shapes each lane l supplies, for row
 // (l & 31) of its operand, one 16-byte chunk of K: chunk 2ks + (l >> 5) of the
@@ -97,6 +102,18 @@ constexpr int64_t kMaxRange = 0x7FFFFFFF;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base, int64_t bytes) {
   const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)n, 0x00020000);
+}
+// The same for a base and size that are the same in every lane of the wave
+// but which the compiler cannot prove uniform (derived from the wave index):
+// taken from the first lane, so the descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_wave(const char* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const int64_t n = bytes < 0 ? 0 : (bytes > kMaxRange ? kMaxRange : bytes);
+  const int nu = __builtin_amdgcn_readfirstlane((int)n);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<char*>(((uint64_t)hi << 32) | lo), (short)0, nu,
+                                           0x00020000);
 }
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
