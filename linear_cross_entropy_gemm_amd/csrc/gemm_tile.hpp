@@ -28,6 +28,8 @@
 // 8 * (v >> 2) + 4 * (l >> 5) + (v & 3) for accumulator element v = 0..15.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace flce {
@@ -648,9 +650,11 @@ __device__ __forceinline__ void lds_barrier() {
 // the wave waits for A_{t+1} and B_{t+1} and for its own LDS reads, and the
 // barrier both publishes them and frees the slots of A_t and B_t; the last
 // sub-step then runs from registers while reading sub-step 0 of step t + 1
-// and issuing B_{t+2}.  The products are added to the values `acc` holds on
-// entry.  Ends with every load landed and a barrier, after which the LDS may
-// be reused by the epilogue.
+// and issuing B_{t+2}.  The last two steps issue no loads (nothing past the
+// K extent is fetched) and wait for everything before their barriers.  The
+// products are added to the values `acc` holds on entry.  Ends with every
+// load landed and a barrier, after which the LDS may be reused by the
+// epilogue.
 template <class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   if (nk <= 0) return;
@@ -675,7 +679,11 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
     a[0][i] = la.read(slot(0), i, 0);
   }
   int sa = 0, sb = 1, sfree = 4;   // slots of A_t, B_t and of B_{t-1} (free)
-  for (int it = 0; it < nk; ++it) {
+  // One K step.  kAhead: step t + 2 exists and is loaded.  The last two steps
+  // run without loads (nothing past the K extent is fetched), so there nothing
+  // newer than B_{t+1} is in flight when the step waits for it.
+  auto step = [&](auto ahead_tag) {
+    constexpr bool kAhead = decltype(ahead_tag)::value;
     const int na = sa + 2 >= kDSlots ? sa + 2 - kDSlots : sa + 2;
     const int nb = sb + 2 >= kDSlots ? sb + 2 - kDSlots : sb + 2;
 #pragma unroll
@@ -684,7 +692,10 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
       const bool last = ks == kDSub - 1;
       if (last) {
         FLCE_FENCE();
-        FLCE_WAIT_VMCNT_LDS(kDLoads);
+        if constexpr (kAhead)
+          FLCE_WAIT_VMCNT_LDS(kDLoads);
+        else
+          FLCE_WAIT_VMCNT_LDS(0);
         __syncthreads();
         FLCE_FENCE();
       }
@@ -702,21 +713,26 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
           a[q][2 * g - 4] = la.read(srca, 2 * g - 4, nks);
           a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
         }
-        if (ks == 0) {
-          la.issue_part(slot_lds(sfree), 2 * g);
-          la.issue_part(slot_lds(sfree), 2 * g + 1);
-        } else if (last) {
-          lb.issue_part(slot_lds(sa), 2 * g);
-          lb.issue_part(slot_lds(sa), 2 * g + 1);
+        if constexpr (kAhead) {
+          if (ks == 0) {
+            la.issue_part(slot_lds(sfree), 2 * g);
+            la.issue_part(slot_lds(sfree), 2 * g + 1);
+          } else if (last) {
+            lb.issue_part(slot_lds(sa), 2 * g);
+            lb.issue_part(slot_lds(sa), 2 * g + 1);
+          }
         }
       }
-      if (ks == 0) la.advance();
+      if (kAhead && ks == 0) la.advance();
     }
-    lb.advance();
+    if (kAhead) lb.advance();
     sfree = sb;
     sa = na;
     sb = nb;
-  }
+  };
+  int it = 0;
+  for (; it < nk - 2; ++it) step(std::true_type{});
+  for (; it < nk; ++it) step(std::false_type{});
   FLCE_FENCE();
   FLCE_WAIT_VMCNT(0);
   __syncthreads();
