@@ -21,7 +21,7 @@ Per workload (c2..c5 of ``synth.CONFIGS``):
   row's log-sum-exp against the stored oracle values;
 * the materialised-logits path at c4 (3.3 GB of bf16 logits, then the
   cross-entropy kernel): loss and n_correct window against the stored oracle
-  values.
+  values, and every stored logit against float32 PyTorch logits.
 """
 import os
 
@@ -196,3 +196,14 @@ def test_full_size_materialised_c4():
     log(f"[full] materialised c4: loss rel {e:.2e}, n_correct {nc} in [{lo}, {hi}]")
     assert e <= 2e-3
     assert lo <= nc <= hi
+    # every stored logit against float32 PyTorch logits (bf16 storage rounding: ~2e-3)
+    WfT = W.float().t().contiguous()
+    num = den = 0.0
+    for r0 in range(0, cfg.N, 2048):
+        a = cfg.multiplier * torch.mm(h[r0:r0 + 2048].float(), WfT)
+        zr = cfg.softcap_T * torch.tanh(a / cfg.softcap_T)
+        num += ((z[r0:r0 + 2048, :cfg.V].float() - zr) ** 2).sum().item()
+        den += (zr ** 2).sum().item()
+    e_z = (num / den) ** 0.5
+    log(f"[full] materialised c4: logits rel {e_z:.2e} against float32 torch logits (all {cfg.N} x {cfg.V})")
+    assert e_z <= 2e-2
