@@ -102,7 +102,11 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
         )
     want_rows = row_outputs or reduction == "none"
     if want_rows and out.loss_rows is None:
-        out.loss_rows, out.lse_rows, out.pred_rows = _row_buffers(N, dev, True, row_outputs)
+        out.loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
+    if row_outputs and out.lse_rows is None:
+        out.lse_rows = torch.empty(N, dtype=torch.float32, device=dev)
+    if row_outputs and out.pred_rows is None:
+        out.pred_rows = torch.empty(N, dtype=torch.int64, device=dev)
     gr = None
     if grad_rows is not None:
         gr = grad_rows.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()

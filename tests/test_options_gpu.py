@@ -187,3 +187,20 @@ def test_autograd_reduction_none():
     log(f"  grad_h {e_gh:.2e} grad_W {e_gW:.2e}")
     assert e_gh <= gt and e_gW <= gt
     assert rows.shape == lab.shape
+
+
+def test_reused_outputs_gain_row_statistics():
+    """An output set first filled without per-row statistics (reduction none:
+    row losses only, valid rows packed) gets its log-sum-exp / argmax
+    buffers when a later call on it asks for them."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c2", 600, 320, 1000, 1.0, 0.37, "mean")
+    log("[options] reused outputs, then row statistics")
+    h, W, lab = to_device(case)
+    o = L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, "none")
+    assert o.loss_rows is not None and o.lse_rows is None and o.pred_rows is None
+    o = L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, "mean", out=o, row_outputs=True)
+    torch.cuda.synchronize()
+    ref = oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, IGN, 1.0, 0.37, "mean")
+    check_rows(case, ref, o.loss_rows, o.lse_rows, o.pred_rows)
