@@ -50,8 +50,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
   const int vbase = tm * kTile + wm * 128 + hi * 4;
   const bool partial = tm * kTile + kTile > p.V;   // only the last vocabulary tile
   const float scale = kCap ? p.mult * p.invT : p.mult;
-  float best[4], sum[4];
-  int bidx[4];
+  float best[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int bidx[4] = {0, 0, 0, 0};
   // One token block (bn) at a time, 64 values per lane, in a loop that is
   // not unrolled: the block's accumulators are copied out first, so the
   // epilogue's code exists once instead of four times (unrolled, it is several
