@@ -64,6 +64,38 @@ def test_plan_invariants(name):
     assert q.as_dict() == p.as_dict()
 
 
+def _split_stats(C, H, Vp, es, s):
+    tiles = -(-C // 256) * -(-H // 256)
+    ksteps = Vp * es // 128
+    per = -(-ksteps // s)
+    real = -(-ksteps // per)
+    waves = -(-(tiles * real) // 256)
+    return tiles * real / (waves * 256), waves, ksteps // real
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_plan_grad_h_split(name):
+    """The grad_h split has the best wave efficiency over the 256 CUs among
+    splits of >= 64 K steps; among equally efficient ones it is the smallest
+    with >= 12 waves of tiles >= 256 K steps long when one exists, else the
+    smallest."""
+    c = synth.CONFIGS[name]
+    dt = L.FLCE_DTYPE_BF16 if c.dtype == "bf16" else L.FLCE_DTYPE_F32
+    es = 2 if c.dtype == "bf16" else 4
+    p = L.flce_plan(c.N, c.H, c.V, dt)
+    ksteps = p.vocab_padded * es // 128
+    cands = [s for s in range(1, 17) if s == 1 or ksteps // s >= 64]
+    stats = {s: _split_stats(p.chunk_rows, c.H, p.vocab_padded, es, s) for s in cands}
+    best = max(e for e, _, _ in stats.values())
+    eff, waves, steps = _split_stats(p.chunk_rows, c.H, p.vocab_padded, es, p.split_k)
+    assert eff >= best - 1e-9
+    long_enough = [s for s in cands if stats[s][0] >= best - 1e-9 and stats[s][1] >= 12 and stats[s][2] >= 256]
+    if long_enough:
+        assert waves >= 12 and steps >= 256
+    # the splits the page shapes get
+    assert p.split_k == {"c1": 1, "c2": 2, "c3": 4, "c4": 8, "c5": 2}[name]
+
+
 def test_plan_budget_shrinks_chunks():
     c = synth.CONFIGS["c4"]
     full = L.flce_plan(c.N, c.H, c.V, 0)
