@@ -254,3 +254,38 @@ def test_outputs_stay_inside_their_buffers(base, N, H, V):
     ref = reference(case)
     gW = bufs["gW"][1].view(torch.float32).view(V, H).cpu().numpy()
     assert rel_fro(gW, ref["grad_W"]) <= tolerances(case.cfg.dtype)[1]
+
+
+def _sweep_cases(n=10, seed=314):
+    """Seeded random shapes: H a multiple of 8 (bf16) or 4 (fp32) and often not
+    of 64 (the K-tail path), V and N ragged, caps from strongly nonlinear to
+    off, both reductions, ignore fractions 0-60%."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f32 = i % 4 == 3
+        H = int(rng.integers(1, 48)) * (4 if f32 else 8)
+        V = int(rng.integers(2, 2200))
+        N = int(rng.integers(1, 900))
+        T = [0.0, 1.0, 3.0, 30.0][(i + i // 4) % 4]
+        m = float(rng.choice([1.0, 0.5, 0.37]))
+        red = ["mean", "sum"][i % 2]
+        frac = float(rng.choice([0.0, 0.05, 0.3, 0.6]))
+        out.append((f"sweep{i}_{'f32' if f32 else 'bf16'}_N{N}_H{H}_V{V}", "c1" if f32 else "c2", N, H, V, T, m, red, frac))
+    return out
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("cid,base,N,H,V,T,m,red,frac", SWEEP, ids=[c[0] for c in SWEEP])
+def test_parity_sweep(cid, base, N, H, V, T, m, red, frac):
+    case = make(base, N, H, V, T, m, red, ignore_frac=frac)
+    c = case.cfg
+    log(f"[sweep] {cid}: T={c.softcap_T} m={c.multiplier} {c.reduction} ignored={int((case.labels == IGN).sum())}")
+    ref = reference(case)
+    o = run_case(case)
+    if ref["valid"].any():
+        check(case, o, ref)
+    else:
+        assert float(o.loss.item()) == 0.0 and not o.grad_W.abs().max().item()
