@@ -88,30 +88,66 @@ __device__ __forceinline__ void softcap_block(f32x16 (&acc)[4][4], int bn, float
   }
 }
 
-// The same on one token block already copied out of the accumulators
-// (x[bm] = acc[bm][bn]).
+// Softcap of one token block already copied out of the accumulators
+// (x[bm] = acc[bm][bn]), z = T tanh(s a) with s = m / T, or m a without a cap.
+// The series of tanh_series is evaluated on the raw accumulator a with the
+// powers of s and the factor T s = m folded into its coefficients:
+//   z = a (m + u Q(u)),  u = a^2,  Q(u) = q1 + u (q2 + u (q3 + u q4)),
+//   q_j = m c_j s^(2j)  (c_j the series coefficients -1/3, 2/15, -17/315, 62/2835),
+// seven operations per value instead of nine (relative error within 1.2e-7 of
+// the float64 tanh over |s a| < 1/4, for m in [-1, 1] and T from 1 to 30);
+// values outside that range take the exponential form, in waves that hold
+// any.
+struct CapSeries {
+  float m, s, T, amax, q1, q2, q3, q4;
+  __device__ __forceinline__ CapSeries(float m_, float invT, float T_) : m(m_), s(m_ * invT), T(T_) {
+    const float s2 = s * s;
+    const float as = __builtin_fabsf(s);
+    amax = as > 0.0f ? kTanhSeriesMax / as : __builtin_inff();
+    q1 = m * (-1.0f / 3.0f) * s2;
+    q2 = m * (2.0f / 15.0f) * (s2 * s2);
+    q3 = m * (-17.0f / 315.0f) * (s2 * s2 * s2);
+    q4 = m * (62.0f / 2835.0f) * ((s2 * s2) * (s2 * s2));
+  }
+};
+
+__device__ __forceinline__ float softcap_series(float a, const CapSeries& c) {
+  const float u = a * a;
+  float q = __builtin_fmaf(c.q4, u, c.q3);
+  q = __builtin_fmaf(q, u, c.q2);
+  q = __builtin_fmaf(q, u, c.q1);
+  return a * __builtin_fmaf(u, q, c.m);
+}
+
+// Every value inside the series range takes the series in both branches, so a
+// row's logits do not depend on which rows share its wave.
 template <bool kCap>
-__device__ __forceinline__ void softcap_cols(f32x16 (&x)[4], float scale, float T) {
+__device__ __forceinline__ void softcap_cols(f32x16 (&x)[4], const CapSeries& c) {
+  if (!kCap) {
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) x[bm][v] *= c.m;
+    return;
+  }
   bool need = false;
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      x[bm][v] *= scale;
-      if (kCap) need |= __builtin_fabsf(x[bm][v]) >= kTanhSeriesMax;
-    }
-  if (kCap) {
-    if (__builtin_amdgcn_ballot_w64(need)) {
+    for (int v = 0; v < 16; ++v) need |= __builtin_fabsf(x[bm][v]) >= c.amax;
+  if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x[bm][v] = T * softcap_tanh(x[bm][v]);
-    } else {
+      for (int v = 0; v < 16; ++v) {
+        const float a = x[bm][v];
+        x[bm][v] = __builtin_fabsf(a) < c.amax ? softcap_series(a, c) : c.T * tanh_exp_form(c.s * a);
+      }
+  } else {
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
+    for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x[bm][v] = T * tanh_series(x[bm][v]);
-    }
+      for (int v = 0; v < 16; ++v) x[bm][v] = softcap_series(x[bm][v], c);
   }
 }
 

@@ -49,7 +49,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
   const int vbase = tm * kTile + wm * 128 + hi * 4;
   const bool partial = tm * kTile + kTile > p.V;   // only the last vocabulary tile
-  const float scale = kCap ? p.mult * p.invT : p.mult;
+  const CapSeries cap(p.mult, p.invT, p.T);
   float best[4] = {kNegInf, kNegInf, kNegInf, kNegInf}, sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   int bidx[4] = {0, 0, 0, 0};
   // One token block (bn) at a time, 64 values per lane, in a loop that is
@@ -72,7 +72,7 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm) x[bm] = acc[bm][3];
     }
-    softcap_cols<kCap>(x, scale, p.T);
+    softcap_cols<kCap>(x, cap);
     // padding columns take no part in the statistics (-inf; exp(-inf) = 0)
     if (partial) {
 #pragma unroll
