@@ -130,12 +130,12 @@ __device__ __forceinline__ void softcap_cols(f32x16 (&x)[4], const CapSeries& c)
       for (int v = 0; v < 16; ++v) x[bm][v] *= c.m;
     return;
   }
-  bool need = false;
+  float mabs = 0.0f;
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) need |= __builtin_fabsf(x[bm][v]) >= c.amax;
-  if (__builtin_amdgcn_ballot_w64(need)) {
+    for (int v = 0; v < 16; ++v) mabs = __builtin_fmaxf(mabs, __builtin_fabsf(x[bm][v]));
+  if (__builtin_amdgcn_ballot_w64(mabs >= c.amax)) {
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll

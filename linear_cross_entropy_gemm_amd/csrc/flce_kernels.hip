@@ -86,7 +86,8 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
     const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
     const bool tok_ok = tok < Ct;
     const int64_t lab64 = tok_ok ? p.labels[tok] : -1;
-    // first maximum: one chain per bm, columns ascending inside each
+    // first maximum: one chain per bm, its maximum first, then the lowest
+    // column holding it (columns descending, so the lowest is written last)
     float mxb[4];
     int axb[4];
 #pragma unroll
@@ -97,12 +98,12 @@ __device__ __forceinline__ void fwd_epilogue(f32x16 (&acc)[4][4], const FwdArgs&
 #pragma unroll
     for (int v = 0; v < 16; ++v)
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
-        const float y = x[bm][v];
-        const bool gt = y > mxb[bm];
-        mxb[bm] = gt ? y : mxb[bm];
-        axb[bm] = gt ? vbase + bm * 32 + 8 * (v >> 2) + (v & 3) : axb[bm];
-      }
+      for (int bm = 0; bm < 4; ++bm) mxb[bm] = __builtin_fmaxf(mxb[bm], x[bm][v]);
+#pragma unroll
+    for (int v = 15; v >= 0; --v)
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm)
+        axb[bm] = x[bm][v] == mxb[bm] ? vbase + bm * 32 + 8 * (v >> 2) + (v & 3) : axb[bm];
     float mx = mxb[0];
     int ax = axb[0];
 #pragma unroll
