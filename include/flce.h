@@ -84,7 +84,8 @@ typedef struct {
 
 /*
  * Compute the chunk plan for a call with these sizes that may use at most
- * `budget_bytes` of workspace (0 = default budget of 16 GiB).  Pure host
+ * `budget_bytes` of workspace (0 = default budget: 16 GiB for the chunk
+ * transients plus the packed copy of the valid rows of h).  Pure host
  * arithmetic; no GPU needed.  Returns FLCE_OK, FLCE_EINVAL (negative sizes,
  * bad dtype, null `out`), FLCE_EUNSUPPORTED (H not a multiple of 8 for bf16 or
  * 4 for fp32; H > 2^21; V above 2^22 - 256 for bf16 or 2^21 - 256 for fp32;

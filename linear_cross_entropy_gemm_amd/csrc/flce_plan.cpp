@@ -5,8 +5,9 @@
 // Memory).  C is the largest multiple of the 256-row tile with
 // C <= ceil(N / 2) whose workspace fits the budget, so every call with N >= 2
 // runs at least two chunks and the full logits never exist.  With 288 GB of
-// HBM per MI355X the default 16 GiB budget never binds for the lm_head shapes
-// of the pages (Muse Glimmer 6656 x 202048, DeepSeek-V3 7168 x 129280).
+// HBM per MI355X the default budget (16 GiB for the transients, plus the packed
+// rows below) never binds for the lm_head shapes of the pages (Muse Glimmer
+// 6656 x 202048, DeepSeek-V3 7168 x 129280).
 //
 // The forward-only plan stores no logits at all (only 12 bytes of partials
 // per token and 256-vocabulary tile), so its chunk is as large as the budget
@@ -110,7 +111,11 @@ int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, bool fw
   const int64_t lim_h = (int64_t(1) << 31) / (int64_t(kRowTile) * 4);
   const int64_t lim_v = (int64_t(1) << 31) / (int64_t(kRowTile) * es) - kVocabTile;
   if (N > (int64_t(1) << 31) - 1 || H > lim_h || V > lim_v) return FLCE_EUNSUPPORTED;
-  if (budget == 0) budget = kDefaultBudget;
+  // The default budget bounds the chunk transients; the packed copy of the
+  // valid rows (as large as h itself) and its row arrays come on top of it.
+  if (budget == 0)
+    budget = kDefaultBudget + size_t(N) * (size_t(H) * size_t(es) + 20) +
+             size_t((N + kPackRows - 1) / kPackRows) * 4 + size_t(256) * 8;
 
   Plan p{};
   p.N = N;

@@ -96,6 +96,17 @@ def test_plan_grad_h_split(name):
     assert p.split_k == {"c1": 1, "c2": 2, "c3": 4, "c4": 8, "c5": 2}[name]
 
 
+def test_default_budget_leaves_room_for_the_packed_rows():
+    """The packed copy of h is as large as h; the default budget bounds the chunk
+    transients and adds the packed rows on top, so a long batch still plans."""
+    N, H, V = 1 << 20, 8192, 128256
+    p = L.flce_plan(N, H, V, L.FLCE_DTYPE_BF16)
+    assert p.n_chunks >= 2 and p.chunk_rows <= (N + 1) // 2
+    packed = N * (H * 2 + 20)
+    assert packed < p.workspace_bytes <= (16 << 30) + packed + (1 << 20)
+    assert L.flce_fwd_workspace_size(N, H, V, L.FLCE_DTYPE_BF16) > packed
+
+
 def test_plan_budget_shrinks_chunks():
     c = synth.CONFIGS["c4"]
     full = L.flce_plan(c.N, c.H, c.V, 0)
