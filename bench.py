@@ -53,9 +53,13 @@ COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: a traffic figure measured on other sources is stale."""
+    """Hash of the sources that decide HBM traffic (the kernels and the
+    chunk / split planner; not the argument checks or the timing facility): a
+    traffic figure measured on other kernels or launch plans is stale."""
     m = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+    files = [f for f in glob.glob(os.path.join(CSRC, "*"))
+             if f.endswith((".hip", ".hpp")) or os.path.basename(f) == "flce_plan.cpp"]
+    for f in sorted(files):
         m.update(os.path.basename(f).encode())
         m.update(open(f, "rb").read())
     return m.hexdigest()[:16]

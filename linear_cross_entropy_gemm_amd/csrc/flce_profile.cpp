@@ -52,14 +52,23 @@ ProfileScope::ProfileScope(int kind, hipStream_t st) : kind_(kind), st_(st) {
   std::lock_guard<std::mutex> g(s.mu);
   a_ = take_event(s);
   b_ = take_event(s);
-  if (a_) hipEventRecord(a_, st_);
+  // a pair that cannot be recorded is not timed: its events go back to the pool
+  if (!a_ || !b_ || hipEventRecord(a_, st_) != hipSuccess) {
+    if (a_) s.pool.push_back(a_);
+    if (b_) s.pool.push_back(b_);
+    a_ = b_ = nullptr;
+  }
 }
 
 ProfileScope::~ProfileScope() {
   if (!a_ || !b_) return;
   State& s = state();
   std::lock_guard<std::mutex> g(s.mu);
-  hipEventRecord(b_, st_);
+  if (hipEventRecord(b_, st_) != hipSuccess) {
+    s.pool.push_back(a_);
+    s.pool.push_back(b_);
+    return;
+  }
   s.pending.push_back({kind_, a_, b_});
 }
 
