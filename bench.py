@@ -127,6 +127,7 @@ def stored_traffic(kernel: str, config: str):
 
 def blas_threads() -> int:
     try:
+        import numpy  # noqa: F401
         from threadpoolctl import threadpool_info
         n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
         if n:
@@ -134,6 +135,36 @@ def blas_threads() -> int:
     except Exception:
         pass
     return len(os.sched_getaffinity(0))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_vendor() -> str:
+    """numpy's BLAS library as threadpoolctl reports it (internal_api and
+    version)."""
+    try:
+        import numpy  # noqa: F401  (loads the BLAS threadpoolctl inspects)
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            p = libs[0]
+            return f"{p.get('internal_api', 'unknown')} {p.get('version') or ''}".strip()
+    except Exception:
+        pass
+    return "unknown"
+
+
+def host_record() -> dict:
+    return {"cores": blas_threads(), "cpu_model": cpu_model(), "blas": blas_vendor(),
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def cpu_baseline(case, n_tokens: int) -> dict:
@@ -149,7 +180,7 @@ def cpu_baseline(case, n_tokens: int) -> dict:
     t0 = time.perf_counter()
     oracle.flce_reference(h, W, lab, synth.IGNORE_INDEX, cfg.softcap_T, cfg.multiplier, cfg.reduction)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", **host_record(), "kind": "oracle",
             "sample": f"first {n} of {cfg.N} tokens of the same seeded inputs, full fp64 forward+backward "
                       f"(loss, argmax, grad_h rows, the sample's [V,H] grad_W) in {dt:.1f} s"}
 
@@ -165,7 +196,7 @@ def cpu_baseline_forward(case, n_tokens: int) -> dict:
     oracle.row_stats(case.h_f32()[:n], case.W_f32(), case.labels[:n], synth.IGNORE_INDEX, cfg.softcap_T,
                      cfg.multiplier)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", **host_record(), "kind": "oracle",
             "sample": f"first {n} of {cfg.N} tokens of the same seeded inputs, fp64 forward "
                       f"(log-sum-exp, label logit, argmax per row) in {dt:.1f} s"}
 

@@ -111,8 +111,9 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype, size_t bu
  *   N, H, V    N >= 0, H >= 1, V >= 1; H % 8 == 0 (bf16) or H % 4 == 0 (fp32).
  *   ignore_index  rows with this label are excluded from the loss, from
  *              n_correct and from the gradients.
- *   softcap_T  logit softcap T; T <= 0 disables the cap.
- *   multiplier output multiplier m, applied to the logits before the cap.
+ *   softcap_T  logit softcap T; T <= 0 disables the cap.  Finite; with a cap,
+ *              1 / T and m / T must be finite as well.
+ *   multiplier output multiplier m, applied to the logits before the cap; finite.
  *   reduction  FLCE_REDUCTION_MEAN or FLCE_REDUCTION_SUM (NONE: flce_fwd_bwd_ex).
  *   loss       [1] fp32, written.
  *   grad_h     [N, H] dtype, written (gradient w.r.t. the caller's h); 16-byte aligned.
@@ -159,7 +160,8 @@ int flce_fwd_bwd(const void* h, const void* W, const int64_t* labels,
  * returned); accumulation into grad_W serves gradient accumulation over
  * micro-batches (SpecForge page, Changes: accumulation prepass).
  * Zero-initialise the struct and set what is needed: every NULL output is
- * skipped, grad_scale = 0 is read as 1.  All pointers are device pointers.
+ * skipped and, with use_grad_scale = 0, the upstream gradient is 1.  All
+ * pointers are device pointers.
  */
 typedef struct {
   float* loss_rows;        /* [N] fp32 out: lse_i - z_{i,label_i} on valid rows, 0 on ignored
@@ -169,17 +171,20 @@ typedef struct {
                               (the predicted token); 8-byte aligned */
   const float* grad_rows;  /* [N] fp32 in: upstream gradient of each row's loss; only with
                               FLCE_REDUCTION_NONE (NULL = 1 for every row) */
-  float grad_scale;        /* upstream gradient of the scalar loss: multiplies grad_h and
-                              this call's grad_W term (0 is read as 1); finite */
+  float grad_scale;        /* upstream gradient of the scalar loss, used when use_grad_scale
+                              is 1: multiplies grad_h and this call's grad_W term (0 gives a
+                              zero grad_h and a zero grad_W term); finite */
   int accumulate_grad_W;   /* 0: grad_W = this call's gradient; 1: grad_W += it (grad_W must
                               hold the running sum on entry) */
+  int use_grad_scale;      /* 0: grad_scale is ignored (upstream gradient 1); 1: it is used */
 } flce_options_t;
 
 /*
  * flce_fwd_bwd with options (may be NULL: then identical to flce_fwd_bwd).
  * Same arguments, workspace and errors as flce_fwd_bwd; `reduction` may also
  * be FLCE_REDUCTION_NONE.  FLCE_EINVAL also for: REDUCTION_NONE without
- * loss_rows, grad_rows with another reduction, a non-finite grad_scale or a
+ * loss_rows, grad_rows with another reduction, use_grad_scale or
+ * accumulate_grad_W other than 0 or 1, a non-finite grad_scale in use or a
  * misaligned row pointer.
  */
 int flce_fwd_bwd_ex(const void* h, const void* W, const int64_t* labels,
@@ -254,6 +259,28 @@ int flce_cross_entropy(const void* logits, int64_t ld_logits, const int64_t* lab
                        const flce_options_t* options);
 
 /*
+ * Upstream-gradient scaling for a training loop whose backward pass runs after
+ * the fused call (DeepSeek-V3 page, Summary: in training with labels the
+ * fused loss is the forward, and autograd's backward hands in the upstream
+ * gradient of the loss only afterwards).  With g the fp32 value at
+ * `grad_scale` (a device pointer, so the host never reads it):
+ *   grad_h_out[i] = grad_h_in[i] * g   for i < n_h, both in h_dtype, computed
+ *                                       in fp32 and rounded once;
+ *   grad_W_out[i] = grad_W_in[i] * g   for i < n_W, read as fp32 (the fused
+ *                                       call's accumulator), written in
+ *                                       w_dtype (the weight's dtype).
+ * Each output may be its input itself (in place; for grad_W only when w_dtype
+ * is fp32) and must not otherwise overlap it.  In place with g == 1 the
+ * grad_h pass writes nothing.  The h pointers may be NULL with n_h = 0, the W
+ * pointers with n_W = 0.  Pointers 16-byte aligned (grad_scale 4-byte).
+ * Enqueued on `stream`; no synchronisation, nothing allocated.  Returns
+ * FLCE_OK, FLCE_EINVAL (null or misaligned pointer, negative size, bad dtype,
+ * partly overlapping buffers) or FLCE_EDEVICE.
+ */
+int flce_scale_grads(const float* grad_scale, const void* grad_h_in, void* grad_h_out, int64_t n_h, int h_dtype,
+                     const float* grad_W_in, void* grad_W_out, int64_t n_W, int w_dtype, hipStream_t stream);
+
+/*
  * Synchronise `stream` and return the device-side status of the last
  * flce_fwd_bwd, flce_fwd_bwd_ex, flce_fwd or flce_cross_entropy that used
  * `workspace`: FLCE_OK or FLCE_ELABEL.  Returns
@@ -282,7 +309,8 @@ enum {
   FLCE_KERNEL_ZERO = 8,         /* zero grad_W when N = 0 */
   FLCE_KERNEL_LOGITS = 9,       /* flce_logits: logits GEMM + softcap into the caller's buffer */
   FLCE_KERNEL_CROSS_ENTROPY = 10,/* flce_cross_entropy: per-row statistics (+ logit gradient) */
-  FLCE_KERNEL_KINDS = 11
+  FLCE_KERNEL_SCALE = 11,       /* flce_scale_grads: upstream-gradient scaling of grad_h / grad_W */
+  FLCE_KERNEL_KINDS = 12
 };
 
 /* Turn event timing on (on != 0) or off for subsequent calls.  Returns FLCE_OK. */

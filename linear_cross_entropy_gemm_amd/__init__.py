@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     flce_profile_read,
     flce_plan,
     flce_read_status,
+    flce_scale_grads,
     flce_strerror,
     flce_workspace_size,
 )
@@ -48,4 +49,6 @@ from .torch_api import (  # noqa: F401
     fwd_bwd,
     linear_cross_entropy,
     logits,
+    read_status,
+    scale_grads,
 )

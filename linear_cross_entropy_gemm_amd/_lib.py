@@ -29,11 +29,11 @@ FLCE_EUNSUPPORTED = 5
 # Every symbol include/flce.h declares.
 EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_fwd_bwd_ex", "flce_fwd_workspace_size",
             "flce_fwd", "flce_logits", "flce_cross_entropy_workspace_size", "flce_cross_entropy",
-            "flce_read_status", "flce_strerror", "flce_profile_enable", "flce_profile_read")
+            "flce_scale_grads", "flce_read_status", "flce_strerror", "flce_profile_enable", "flce_profile_read")
 
 # Kernel kinds of the per-kernel timing facility (index order of the arrays).
 KERNEL_KINDS = ("label_scan", "fwd_logits", "row_merge", "grad_logits", "grad_h", "grad_h_reduce",
-                "grad_W", "finalize", "zero", "logits", "cross_entropy")
+                "grad_W", "finalize", "zero", "logits", "cross_entropy", "scale")
 
 
 class flce_plan_t(ctypes.Structure):
@@ -60,6 +60,7 @@ class flce_options_t(ctypes.Structure):
         ("grad_rows", ctypes.c_void_p),
         ("grad_scale", ctypes.c_float),
         ("accumulate_grad_W", ctypes.c_int),
+        ("use_grad_scale", ctypes.c_int),
     ]
 
 
@@ -108,6 +109,8 @@ def _load() -> ctypes.CDLL:
     lib.flce_cross_entropy.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp, vp, vp, i64, vp, i32, vp, sz,
                                        ctypes.POINTER(flce_options_t)]
     lib.flce_cross_entropy.restype = i32
+    lib.flce_scale_grads.argtypes = [vp, vp, vp, i64, i32, vp, vp, i64, i32, vp]
+    lib.flce_scale_grads.restype = i32
     lib.flce_read_status.argtypes = [vp, vp]
     lib.flce_read_status.restype = i32
     lib.flce_strerror.argtypes = [i32]
@@ -185,6 +188,14 @@ def flce_cross_entropy(logits: int, ld_logits: int, labels: int, N: int, V: int,
     return int(_lib.flce_cross_entropy(logits, ld_logits, labels, N, V, ignore_index, reduction, loss,
                                        n_correct, grad_logits, ld_grad, stream, dtype, workspace,
                                        workspace_bytes, _opts(options)))
+
+
+def flce_scale_grads(grad_scale: int, grad_h_in, grad_h_out, n_h: int, h_dtype: int, grad_W_in, grad_W_out,
+                     n_W: int, w_dtype: int, stream: int) -> int:
+    """Raw call: grad_h_out = grad_h_in * g and grad_W_out = grad_W_in * g (g at
+    device address grad_scale); returns the C return code."""
+    return int(_lib.flce_scale_grads(grad_scale, grad_h_in, grad_h_out, n_h, h_dtype, grad_W_in, grad_W_out,
+                                     n_W, w_dtype, stream))
 
 
 def flce_read_status(workspace: int, stream: int) -> int:

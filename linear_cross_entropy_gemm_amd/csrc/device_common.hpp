@@ -27,21 +27,22 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * kLog2e);
 }
 
-// tanh for the logit softcap, written from the mathematics:
-//  * |x| < 0.25: the odd Maclaurin series x - x^3/3 + 2x^5/15 - 17x^7/315
-//    + 62x^9/2835 (the first omitted term is below 1e-8 relative there);
-//  * otherwise tanh|x| = 1 - 2 / (e^{2|x|} + 1), which saturates to 1 as
-//    e^{2|x|} overflows, with the sign restored.
-// Relative error is below 1e-6 over the whole range (tested against fp64).
-__host__ __device__ __forceinline__ float tanh_series(float x) {
-  const float x2 = x * x;
-  float p = 62.0f / 2835.0f;
-  p = __builtin_fmaf(p, x2, -17.0f / 315.0f);
-  p = __builtin_fmaf(p, x2, 2.0f / 15.0f);
-  p = __builtin_fmaf(p, x2, -1.0f / 3.0f);
-  p = p * x2;
-  return __builtin_fmaf(x, p, x);
-}
+// Logit softcap z = T tanh(m a / T) (Muse Glimmer page, Details > Softcap),
+// written from the mathematics on the raw accumulator a:
+//  * |m a / T| < 1/4: the odd Maclaurin series of tanh, x - x^3/3 + 2x^5/15
+//    - 17x^7/315 + 62x^9/2835 (the first omitted term, 1382x^11/155925, is
+//    below 1e-8 relative there), with the powers of s = m / T and the factor
+//    T s = m folded into its coefficients:
+//      z = a (m + u Q(u)),  u = a^2,  Q(u) = q1 + u (q2 + u (q3 + u q4)),
+//      q_j = m c_j s^(2j)  (c_j = -1/3, 2/15, -17/315, 62/2835),
+//    seven operations per value;
+//  * otherwise tanh|x| = 1 - 2 / (e^{2|x|} + 1) with the sign restored, which
+//    saturates to 1 as e^{2|x|} overflows.
+// Without a cap, z = m a.  When |s| exceeds 2^12 the folded coefficients
+// would overflow (s^8 near |s| = 2^16), so the series is evaluated unfolded on
+// x = s a instead, with the same range switch.  tests/test_softcap_host.py checks these functions on
+// the host against float64 tanh; the GPU softcap test checks the kernels'
+// logits (hardware exp2 and reciprocal) the same way.
 __host__ __device__ __forceinline__ float tanh_exp_form(float x) {
   const float ax = __builtin_fabsf(x);
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -54,55 +55,30 @@ __host__ __device__ __forceinline__ float tanh_exp_form(float x) {
   return __builtin_copysignf(r, x);
 }
 constexpr float kTanhSeriesMax = 0.25f;
-__host__ __device__ __forceinline__ float softcap_tanh(float x) {
-  return __builtin_fabsf(x) < kTanhSeriesMax ? tanh_series(x) : tanh_exp_form(x);
+constexpr float kSeriesScaleMax = 4096.0f;
+
+// The series on x itself: x + x^3 P(x^2).
+__host__ __device__ __forceinline__ float tanh_series(float x) {
+  const float x2 = x * x;
+  float p = __builtin_fmaf(62.0f / 2835.0f, x2, -17.0f / 315.0f);
+  p = __builtin_fmaf(p, x2, 2.0f / 15.0f);
+  p = __builtin_fmaf(p, x2, -1.0f / 3.0f);
+  return __builtin_fmaf(x, p * x2, x);
 }
 
-// Logits of one token block bn of a wave's 4 x 4 accumulator blocks:
-// z = T tanh(m a / T) (kCap) or m a, in place; `scale` is m / T (kCap) or m.
-// The series serves when every lane's |m a / T| < 1/4 (the usual case for
-// lm_head logits under a large cap); otherwise the whole wave takes the
-// exponential form.
-template <bool kCap>
-__device__ __forceinline__ void softcap_block(f32x16 (&acc)[4][4], int bn, float scale, float T) {
-  bool need = false;
-#pragma unroll
-  for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      acc[bm][bn][v] *= scale;
-      if (kCap) need |= __builtin_fabsf(acc[bm][bn][v]) >= kTanhSeriesMax;
-    }
-  if (kCap) {
-    if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[bm][bn][v] = T * softcap_tanh(acc[bm][bn][v]);
-    } else {
-#pragma unroll
-      for (int bm = 0; bm < 4; ++bm)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[bm][bn][v] = T * tanh_series(acc[bm][bn][v]);
-    }
-  }
-}
-
-// Softcap of one token block already copied out of the accumulators
-// (x[bm] = acc[bm][bn]), z = T tanh(s a) with s = m / T, or m a without a cap.
-// The series of tanh_series is evaluated on the raw accumulator a with the
-// powers of s and the factor T s = m folded into its coefficients:
-//   z = a (m + u Q(u)),  u = a^2,  Q(u) = q1 + u (q2 + u (q3 + u q4)),
-//   q_j = m c_j s^(2j)  (c_j the series coefficients -1/3, 2/15, -17/315, 62/2835),
-// seven operations per value instead of nine (relative error within 1.2e-7 of
-// the float64 tanh over |s a| < 1/4, for m in [-1, 1] and T from 1 to 30);
-// values outside that range take the exponential form, in waves that hold
-// any.
 struct CapSeries {
   float m, s, T, amax, q1, q2, q3, q4;
-  __device__ __forceinline__ CapSeries(float m_, float invT, float T_) : m(m_), s(m_ * invT), T(T_) {
-    const float s2 = s * s;
+  bool unfolded;   // |s| > 2^12: the series runs on x = s a (amax = 0 sends every value there)
+  __host__ __device__ __forceinline__ CapSeries(float m_, float invT, float T_)
+      : m(m_), s(m_ * invT), T(T_), unfolded(false) {
     const float as = __builtin_fabsf(s);
+    if (as > kSeriesScaleMax) {
+      unfolded = true;
+      amax = 0.0f;
+      q1 = q2 = q3 = q4 = 0.0f;
+      return;
+    }
+    const float s2 = s * s;
     amax = as > 0.0f ? kTanhSeriesMax / as : __builtin_inff();
     q1 = m * (-1.0f / 3.0f) * s2;
     q2 = m * (2.0f / 15.0f) * (s2 * s2);
@@ -111,7 +87,7 @@ struct CapSeries {
   }
 };
 
-__device__ __forceinline__ float softcap_series(float a, const CapSeries& c) {
+__host__ __device__ __forceinline__ float softcap_series(float a, const CapSeries& c) {
   const float u = a * a;
   float q = __builtin_fmaf(c.q4, u, c.q3);
   q = __builtin_fmaf(q, u, c.q2);
@@ -119,8 +95,21 @@ __device__ __forceinline__ float softcap_series(float a, const CapSeries& c) {
   return a * __builtin_fmaf(u, q, c.m);
 }
 
-// Every value inside the series range takes the series in both branches, so a
-// row's logits do not depend on which rows share its wave.
+// The capped logit of one raw accumulator value: the rule softcap_cols
+// applies to every value, whichever of its branches a wave takes.
+__host__ __device__ __forceinline__ float softcap_value(float a, const CapSeries& c) {
+  if (c.unfolded) {
+    const float x = c.s * a;
+    return c.T * (__builtin_fabsf(x) < kTanhSeriesMax ? tanh_series(x) : tanh_exp_form(x));
+  }
+  return __builtin_fabsf(a) < c.amax ? softcap_series(a, c) : c.T * tanh_exp_form(c.s * a);
+}
+
+// Softcap of one token block already copied out of the accumulators
+// (x[bm] = acc[bm][bn]), in place.  Waves whose values all lie inside the
+// series range skip the range test; every value inside the range takes the
+// series in both branches, so a row's logits do not depend on which rows
+// share its wave.
 template <bool kCap>
 __device__ __forceinline__ void softcap_cols(f32x16 (&x)[4], const CapSeries& c) {
   if (!kCap) {
@@ -139,10 +128,7 @@ __device__ __forceinline__ void softcap_cols(f32x16 (&x)[4], const CapSeries& c)
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float a = x[bm][v];
-        x[bm][v] = __builtin_fabsf(a) < c.amax ? softcap_series(a, c) : c.T * tanh_exp_form(c.s * a);
-      }
+      for (int v = 0; v < 16; ++v) x[bm][v] = softcap_value(x[bm][v], c);
   } else {
 #pragma unroll
     for (int bm = 0; bm < 4; ++bm)

@@ -38,19 +38,32 @@ extern "C" size_t flce_fwd_workspace_size(int64_t N, int64_t H, int64_t V, int d
 
 namespace {
 
+// T and m finite, and with a cap 1 / T and m / T finite too (the kernels
+// scale by both).
+bool scalars_ok(float softcap_T, float multiplier) {
+  if (!std::isfinite(softcap_T) || !std::isfinite(multiplier)) return false;
+  if (softcap_T > 0.0f && (!std::isfinite(1.0f / softcap_T) || !std::isfinite(multiplier / softcap_T)))
+    return false;
+  return true;
+}
+
+}  // namespace
+
+namespace flce {
+
 // Host-side checks shared by the entry points; nothing is enqueued before
 // they pass.  grad_h / grad_W are checked only when `with_grads`.
-int validate(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
-             float softcap_T, float multiplier, int reduction, const float* loss, const void* grad_h,
-             const float* grad_W, const int64_t* n_correct, int dtype, const void* workspace,
-             const flce_options_t* o, bool with_grads) {
+int validate_call(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+                  float softcap_T, float multiplier, int reduction, const float* loss, const void* grad_h,
+                  const float* grad_W, const int64_t* n_correct, int dtype, const void* workspace,
+                  const flce_options_t* o, bool with_grads) {
   if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
   if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM && reduction != FLCE_REDUCTION_NONE)
     return FLCE_EINVAL;
   if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
   if (!W || !loss || !workspace) return FLCE_EINVAL;
   if (N > 0 && (!h || !labels)) return FLCE_EINVAL;
-  if (std::isnan(softcap_T) || std::isinf(softcap_T) || !std::isfinite(multiplier)) return FLCE_EINVAL;
+  if (!scalars_ok(softcap_T, multiplier)) return FLCE_EINVAL;
   if (!aligned(W, 16) || !aligned(loss, 4) || !aligned(workspace, 256)) return FLCE_EINVAL;
   if (N > 0 && (!aligned(h, 16) || !aligned(labels, 8))) return FLCE_EINVAL;
   if (n_correct && !aligned(n_correct, 8)) return FLCE_EINVAL;
@@ -65,18 +78,19 @@ int validate(const void* h, const void* W, const int64_t* labels, int64_t N, int
     if (o->pred_rows && !aligned(o->pred_rows, 8)) return FLCE_EINVAL;
     if (with_grads) {
       if (o->grad_rows && (reduction != FLCE_REDUCTION_NONE || !aligned(o->grad_rows, 4))) return FLCE_EINVAL;
-      if (!std::isfinite(o->grad_scale)) return FLCE_EINVAL;
+      if (o->use_grad_scale != 0 && o->use_grad_scale != 1) return FLCE_EINVAL;
+      if (o->use_grad_scale && !std::isfinite(o->grad_scale)) return FLCE_EINVAL;
       if (o->accumulate_grad_W != 0 && o->accumulate_grad_W != 1) return FLCE_EINVAL;
     }
   }
   return FLCE_OK;
 }
 
-flce::CallArgs make_args(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
-                         int64_t V, int64_t ignore_index, float softcap_T, float multiplier,
-                         int reduction, float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
-                         int dtype, void* workspace, const flce_options_t* o, bool fwd_only) {
-  flce::CallArgs a;
+CallArgs make_call_args(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+                        int64_t ignore_index, float softcap_T, float multiplier, int reduction, float* loss,
+                        void* grad_h, float* grad_W, int64_t* n_correct, int dtype, void* workspace,
+                        const flce_options_t* o, bool fwd_only) {
+  CallArgs a;
   a.h = h;
   a.W = W;
   a.labels = labels;
@@ -100,28 +114,28 @@ flce::CallArgs make_args(const void* h, const void* W, const int64_t* labels, in
     a.pred_rows = o->pred_rows;
     if (!fwd_only) {
       a.grad_rows = o->grad_rows;
-      a.grad_scale = o->grad_scale == 0.0f ? 1.0f : o->grad_scale;
+      a.grad_scale = o->use_grad_scale ? o->grad_scale : 1.0f;
       a.accumulate_grad_W = o->accumulate_grad_W != 0;
     }
   }
   return a;
 }
 
-}  // namespace
+}  // namespace flce
 
 extern "C" int flce_fwd_bwd_ex(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
                                int64_t V, int64_t ignore_index, float softcap_T, float multiplier,
                                int reduction, float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
                                hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes,
                                const flce_options_t* options) {
-  int rc = validate(h, W, labels, N, H, V, softcap_T, multiplier, reduction, loss, grad_h, grad_W,
+  int rc = flce::validate_call(h, W, labels, N, H, V, softcap_T, multiplier, reduction, loss, grad_h, grad_W,
                     n_correct, dtype, workspace, options, true);
   if (rc != FLCE_OK) return rc;
   Plan p;
   rc = flce::make_plan(N, H, V, dtype, workspace_bytes, false, &p);
   if (rc != FLCE_OK) return rc;
   if (p.total > workspace_bytes) return FLCE_EWORKSPACE;
-  const flce::CallArgs a = make_args(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
+  const flce::CallArgs a = flce::make_call_args(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
                                      loss, grad_h, grad_W, n_correct, dtype, workspace, options, false);
   return flce::run_call(a, p, stream);
 }
@@ -139,14 +153,14 @@ extern "C" int flce_fwd(const void* h, const void* W, const int64_t* labels, int
                         int64_t V, int64_t ignore_index, float softcap_T, float multiplier, int reduction,
                         float* loss, int64_t* n_correct, hipStream_t stream, int dtype, void* workspace,
                         size_t workspace_bytes, const flce_options_t* options) {
-  int rc = validate(h, W, labels, N, H, V, softcap_T, multiplier, reduction, loss, nullptr, nullptr,
+  int rc = flce::validate_call(h, W, labels, N, H, V, softcap_T, multiplier, reduction, loss, nullptr, nullptr,
                     n_correct, dtype, workspace, options, false);
   if (rc != FLCE_OK) return rc;
   Plan p;
   rc = flce::make_plan(N, H, V, dtype, workspace_bytes, true, &p);
   if (rc != FLCE_OK) return rc;
   if (p.total > workspace_bytes) return FLCE_EWORKSPACE;
-  const flce::CallArgs a = make_args(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
+  const flce::CallArgs a = flce::make_call_args(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier, reduction,
                                      loss, nullptr, nullptr, n_correct, dtype, workspace, options, true);
   return flce::run_call(a, p, stream);
 }
@@ -172,7 +186,7 @@ extern "C" int flce_logits(const void* h, const void* W, int64_t N, int64_t H, i
   if (dtype != FLCE_DTYPE_BF16 && dtype != FLCE_DTYPE_F32) return FLCE_EINVAL;
   if (N < 0 || H < 1 || V < 1) return FLCE_EINVAL;
   if (!W || !aligned(W, 16)) return FLCE_EINVAL;
-  if (std::isnan(softcap_T) || std::isinf(softcap_T) || !std::isfinite(multiplier)) return FLCE_EINVAL;
+  if (!scalars_ok(softcap_T, multiplier)) return FLCE_EINVAL;
   const int64_t es = dtype == FLCE_DTYPE_BF16 ? 2 : 4;
   if (N > 0 && (!h || !aligned(h, 16) || !rows_ok(logits, ld_logits, V, es))) return FLCE_EINVAL;
   int rc = check_shape(N, H, V, dtype);
@@ -220,7 +234,8 @@ extern "C" int flce_cross_entropy(const void* logits, int64_t ld_logits, const i
     if (o->lse_rows && !aligned(o->lse_rows, 4)) return FLCE_EINVAL;
     if (o->pred_rows && !aligned(o->pred_rows, 8)) return FLCE_EINVAL;
     if (o->grad_rows && (reduction != FLCE_REDUCTION_NONE || !aligned(o->grad_rows, 4))) return FLCE_EINVAL;
-    if (!std::isfinite(o->grad_scale)) return FLCE_EINVAL;
+    if (o->use_grad_scale != 0 && o->use_grad_scale != 1) return FLCE_EINVAL;
+    if (o->use_grad_scale && !std::isfinite(o->grad_scale)) return FLCE_EINVAL;
   }
   if (workspace_bytes < flce::cross_entropy_workspace(N)) return FLCE_EWORKSPACE;
   flce::CeCallArgs a;
@@ -242,7 +257,7 @@ extern "C" int flce_cross_entropy(const void* logits, int64_t ld_logits, const i
     a.lse_rows = o->lse_rows;
     a.pred_rows = o->pred_rows;
     a.grad_rows = o->grad_rows;
-    a.grad_scale = o->grad_scale == 0.0f ? 1.0f : o->grad_scale;
+    a.grad_scale = o->use_grad_scale ? o->grad_scale : 1.0f;
   }
   return flce::run_cross_entropy(a, stream);
 }

@@ -2,7 +2,7 @@
 // (flce_plan.cpp) and the kernels (flce_kernels.hip).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -67,6 +67,17 @@ struct CallArgs {
 
 // Enqueue the whole call on `stream`.  Returns FLCE_OK or FLCE_EDEVICE.
 int run_call(const CallArgs& a, const Plan& pl, hipStream_t stream);
+
+// Host-side argument checks of the fused entry points (grad_h / grad_W only
+// when `with_grads`) and the call description they hand to run_call.
+int validate_call(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+                  float softcap_T, float multiplier, int reduction, const float* loss, const void* grad_h,
+                  const float* grad_W, const int64_t* n_correct, int dtype, const void* workspace,
+                  const flce_options_t* o, bool with_grads);
+CallArgs make_call_args(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+                        int64_t ignore_index, float softcap_T, float multiplier, int reduction, float* loss,
+                        void* grad_h, float* grad_W, int64_t* n_correct, int dtype, void* workspace,
+                        const flce_options_t* o, bool fwd_only);
 
 // Materialised-logits path (flce_logits / flce_cross_entropy).
 struct LogitsCallArgs {

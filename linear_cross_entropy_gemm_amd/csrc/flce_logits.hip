@@ -46,16 +46,21 @@ struct CeArgs {
 
 // Store the capped logits of one token block to the caller's row; in the
 // last vocabulary tile, vectors that cross V are stored element by element.
+// The softcap is the fused forward's (softcap_cols), so both paths produce
+// the same logits bit for bit.
 template <typename T, bool kCap>
 __device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], const LogitsArgs& p, int tm, int tn) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1, lo = lane & 31, hi = lane >> 5;
   const int vbase = tm * kTile + wm * 128 + hi * 4;
   const bool partial = tm * kTile + kTile > p.V;
-  const float scale = kCap ? p.mult * p.invT : p.mult;
+  const CapSeries cap(p.mult, p.invT, p.T);
 #pragma unroll
   for (int bn = 0; bn < 4; ++bn) {
-    softcap_block<kCap>(acc, bn, scale, p.T);
+    f32x16 x[4];
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm) x[bm] = acc[bm][bn];
+    softcap_cols<kCap>(x, cap);
     const int tok = tn * kTile + wn * 128 + bn * 32 + lo;
     if (tok >= p.N) continue;
     T* zr = reinterpret_cast<T*>(static_cast<char*>(p.out) + (int64_t)tok * p.ldo);
@@ -64,8 +69,8 @@ __device__ __forceinline__ void logits_epilogue(f32x16 (&acc)[4][4], const Logit
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = vbase + bm * 32 + 8 * i;
-        const float x0 = acc[bm][bn][4 * i], x1 = acc[bm][bn][4 * i + 1];
-        const float x2 = acc[bm][bn][4 * i + 2], x3 = acc[bm][bn][4 * i + 3];
+        const float x0 = x[bm][4 * i], x1 = x[bm][4 * i + 1];
+        const float x2 = x[bm][4 * i + 2], x3 = x[bm][4 * i + 3];
         if (!partial || c + 3 < p.V) {
           store4(zr + c, x0, x1, x2, x3);
         } else {

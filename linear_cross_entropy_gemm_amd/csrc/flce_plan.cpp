@@ -135,26 +135,48 @@ int make_plan(int64_t N, int64_t H, int64_t V, int dtype, size_t budget, bool fw
     return FLCE_OK;
   }
   const int64_t top = fwd_only ? N : (N + 1) / 2;
-  int64_t c = top < kRowTile ? top : top / kRowTile * kRowTile;
-  for (;;) {
+  const int64_t ksteps = p.Vp * es / 128;
+  // The planner's chunk and grad_h split, or, when the budget binds, fewer
+  // splits (smaller fp32 partials) before a smaller chunk.
+  auto fits = [&](int64_t c) {
     p.C = c;
     p.n_chunks = (N + c - 1) / c;
-    p.split_k = choose_split(c, H, p.Vp, es);
-    layout(&p);
-    if (p.total <= budget) {
+    const int64_t pick = choose_split(c, H, p.Vp, es);
+    for (int64_t s = pick; s >= 1; --s) {
+      const int64_t per = (ksteps + s - 1) / s;
+      const int64_t real = (ksteps + per - 1) / per;
+      if (s < pick && real == p.split_k) continue;   // same split as the last one tried
+      p.split_k = real;
+      layout(&p);
+      if (p.total <= budget) return true;
+      if (fwd_only) break;   // no partials: the split does not change the size
+    }
+    return false;
+  };
+  // Whether some split fits depends on c alone (with one split the
+  // workspace grows with c), so the largest fitting chunk is found by
+  // bisection: multiples of the row tile first, then halving below one tile.
+  int64_t c = top < kRowTile ? top : top / kRowTile * kRowTile;
+  if (fits(c)) {
+    *out = p;
+    return FLCE_OK;
+  }
+  if (c > kRowTile) {
+    int64_t lo = 0, hi = c / kRowTile;   // tiles: hi does not fit; lo fits (0: none known)
+    while (hi - lo > 1) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (fits(mid * kRowTile))
+        lo = mid;
+      else
+        hi = mid;
+    }
+    if (lo > 0 && fits(lo * kRowTile)) {
       *out = p;
       return FLCE_OK;
     }
-    if (c <= kRowTile) break;
-    c -= kRowTile;
   }
-  // below one row tile: halve until it fits
   for (c = std::min<int64_t>(c, kRowTile) / 2; c >= 1; c /= 2) {
-    p.C = c;
-    p.n_chunks = (N + c - 1) / c;
-    p.split_k = choose_split(c, H, p.Vp, es);
-    layout(&p);
-    if (p.total <= budget) {
+    if (fits(c)) {
       *out = p;
       return FLCE_OK;
     }

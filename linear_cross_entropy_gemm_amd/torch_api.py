@@ -56,6 +56,18 @@ def _prepare(h, W, labels, reduction):
     return h2, W.contiguous(), lab
 
 
+def _workspace(workspace: Optional[torch.Tensor], nbytes: int, dev) -> torch.Tensor:
+    """The caller's workspace (a contiguous uint8 tensor of at least ``nbytes``
+    on the device of h), or a new one."""
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on the device of h")
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, this call needs {nbytes}")
+    return workspace
+
+
 def _row_buffers(N: int, dev, want_loss: bool, want_stats: bool):
     """Per-row loss (reduction "none" or row_outputs) and per-row log-sum-exp /
     argmax (row_outputs only: asking for them keeps the ignored rows in the
@@ -66,18 +78,51 @@ def _row_buffers(N: int, dev, want_loss: bool, want_stats: bool):
     return loss_rows, torch.empty(N, dtype=torch.float32, device=dev), torch.empty(N, dtype=torch.int64, device=dev)
 
 
+def _check_out(out: "FlceOutputs", N: int, H: int, V: int, h_dtype, dev) -> None:
+    """Every buffer of a reused output set must match this call before its
+    address reaches the kernels: shape, dtype, device and contiguity."""
+    want = [("loss", out.loss, (), torch.float32), ("grad_h", out.grad_h, None, h_dtype),
+            ("grad_W", out.grad_W, (V, H), torch.float32), ("n_correct", out.n_correct, (), torch.int64),
+            ("loss_rows", out.loss_rows, (N,), torch.float32), ("lse_rows", out.lse_rows, (N,), torch.float32),
+            ("pred_rows", out.pred_rows, (N,), torch.int64)]
+    for name, t, shape, dt in want:
+        if t is None:
+            if name in ("loss", "grad_h", "grad_W", "n_correct"):
+                raise ValueError(f"out.{name} is missing")
+            continue
+        if name == "grad_h":
+            ok_shape = t.numel() == N * H and (t.dim() == 0 or t.shape[-1] == H or N * H == 0)
+        else:
+            ok_shape = tuple(t.shape) == shape
+        if not ok_shape:
+            raise ValueError(f"out.{name} has shape {tuple(t.shape)}, this call needs "
+                             f"{(N, H) if shape is None else shape}")
+        if t.dtype != dt:
+            raise ValueError(f"out.{name} is {t.dtype}, this call needs {dt}")
+        if t.device != dev:
+            raise ValueError(f"out.{name} is on {t.device}, this call runs on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"out.{name} must be contiguous")
+
+
 def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
             softcap: Optional[float] = None, multiplier: float = 1.0, reduction: str = "mean",
             workspace: Optional[torch.Tensor] = None, out: Optional[FlceOutputs] = None,
-            check: bool = True, *, grad_rows: Optional[torch.Tensor] = None, grad_scale: float = 1.0,
-            accumulate_grad_W: bool = False, row_outputs: bool = False) -> FlceOutputs:
+            check: bool = True, *, grad_rows: Optional[torch.Tensor] = None,
+            grad_scale: Optional[float] = None, accumulate_grad_W: bool = False,
+            row_outputs: bool = False) -> FlceOutputs:
     """One call of ``flce_fwd_bwd_ex`` on torch's current stream.
 
     ``h`` [..., H] is flattened to [N, H] and ``grad_h`` restored to its shape
     (SpecForge PR 1007, Changes: flatten rows for the vocabulary projection,
-    then restore the output shape).  ``grad_rows`` (reduction "none") and
-    ``grad_scale`` are upstream gradients; with ``accumulate_grad_W`` the call
-    adds its weight gradient to ``out.grad_W``."""
+    then restore the output shape); with reduction "none" the per-row losses
+    take the shape of ``labels``.  ``grad_rows`` (reduction "none") and
+    ``grad_scale`` (None: 1; 0 gives zero gradients) are upstream gradients;
+    with ``accumulate_grad_W`` the call adds its weight gradient to
+    ``out.grad_W``.  A reused ``out`` must match the call (checked before the
+    launch).  ``check`` synchronises the stream and raises on out-of-range
+    labels; without it nothing waits and ``read_status(workspace)`` reports
+    them later."""
     h2, Wc, lab = _prepare(h, W, labels, reduction)
     shape = h.shape
     N, H = h2.shape
@@ -88,8 +133,7 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     if ws_bytes == 0:
         raise _lib.FlceError(_lib.FLCE_EUNSUPPORTED, "flce_workspace_size")
     dev = h.device
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     if accumulate_grad_W and out is None:
         raise ValueError("accumulate_grad_W needs out.grad_W holding the running sum")
     if out is None:
@@ -100,6 +144,10 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
             n_correct=torch.empty((), dtype=torch.int64, device=dev),
             workspace=workspace,
         )
+    else:
+        if out.loss_rows is not None:
+            out.loss_rows = out.loss_rows.reshape(-1)
+        _check_out(out, N, H, V, h.dtype, dev)
     want_rows = row_outputs or reduction == "none"
     if want_rows and out.loss_rows is None:
         out.loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
@@ -116,7 +164,8 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
         loss_rows=_ptr(out.loss_rows) if want_rows else None,
         lse_rows=_ptr(out.lse_rows) if row_outputs else None,
         pred_rows=_ptr(out.pred_rows) if row_outputs else None,
-        grad_rows=_ptr(gr), grad_scale=float(grad_scale), accumulate_grad_W=1 if accumulate_grad_W else 0)
+        grad_rows=_ptr(gr), grad_scale=float(grad_scale) if grad_scale is not None else 0.0,
+        accumulate_grad_W=1 if accumulate_grad_W else 0, use_grad_scale=0 if grad_scale is None else 1)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = _lib.flce_fwd_bwd_ex(_ptr(h2), _ptr(Wc), _ptr(lab), N, H, V, int(ignore_index),
                               float(softcap) if softcap else 0.0, float(multiplier), red,
@@ -129,8 +178,19 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
         if st != _lib.FLCE_OK:
             raise _lib.FlceError(st, "flce_fwd_bwd_ex (device status)")
     out.grad_h = out.grad_h.reshape(shape)
+    if out.loss_rows is not None and reduction == "none":
+        out.loss_rows = out.loss_rows.reshape(labels.shape)
     out.workspace = workspace
     return out
+
+
+def read_status(workspace: torch.Tensor) -> None:
+    """Synchronise torch's current stream and raise if the last call that used
+    ``workspace`` found a label outside [0, V) that is not ignore_index."""
+    stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    st = _lib.flce_read_status(_ptr(workspace), stream)
+    if st != _lib.FLCE_OK:
+        raise _lib.FlceError(st, "device status")
 
 
 def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100,
@@ -147,8 +207,7 @@ def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     if ws_bytes == 0:
         raise _lib.FlceError(_lib.FLCE_EUNSUPPORTED, "flce_fwd_workspace_size")
     dev = h.device
-    if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, ws_bytes, dev)
     loss_rows, lse_rows, pred_rows = _row_buffers(N, dev, reduction == "none", row_outputs)
     res = FlceForward(loss=torch.empty((), dtype=torch.float32, device=dev),
                       n_correct=torch.empty((), dtype=torch.int64, device=dev), workspace=workspace,
@@ -165,6 +224,8 @@ def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
         st = _lib.flce_read_status(_ptr(workspace), stream)
         if st != _lib.FLCE_OK:
             raise _lib.FlceError(st, "flce_fwd (device status)")
+    if reduction == "none":
+        res.loss_rows = res.loss_rows.reshape(labels.shape)
     return res
 
 
@@ -211,7 +272,8 @@ class CrossEntropyOutputs:
 
 def cross_entropy(z: torch.Tensor, labels: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
                   grad: bool = False, in_place: bool = False, grad_rows: Optional[torch.Tensor] = None,
-                  grad_scale: float = 1.0, row_outputs: bool = False, check: bool = True) -> CrossEntropyOutputs:
+                  grad_scale: Optional[float] = None, row_outputs: bool = False,
+                  check: bool = True) -> CrossEntropyOutputs:
     """Cross-entropy of given logits ``z`` [N, V] (``flce_cross_entropy``),
     optionally with d loss / d z (written into z itself with ``in_place``).
     z may be a row-padded view (row stride a multiple of 16 bytes)."""
@@ -236,7 +298,9 @@ def cross_entropy(z: torch.Tensor, labels: torch.Tensor, ignore_index: int = -10
     if grad_rows is not None:
         gr = grad_rows.reshape(-1).to(device=dev, dtype=torch.float32).contiguous()
     opts = _lib.flce_options_t(loss_rows=_ptr(res.loss_rows), lse_rows=_ptr(res.lse_rows),
-                               pred_rows=_ptr(res.pred_rows), grad_rows=_ptr(gr), grad_scale=float(grad_scale))
+                               pred_rows=_ptr(res.pred_rows), grad_rows=_ptr(gr),
+                               grad_scale=float(grad_scale) if grad_scale is not None else 0.0,
+                               use_grad_scale=0 if grad_scale is None else 1)
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = _lib.flce_cross_entropy(_ptr(z), z.stride(0), _ptr(lab), N, V, int(ignore_index), _REDUCTIONS[reduction],
                                  _ptr(res.loss), _ptr(res.n_correct), _ptr(g), g.stride(0) if g is not None else 0,
@@ -250,44 +314,78 @@ def cross_entropy(z: torch.Tensor, labels: torch.Tensor, ignore_index: int = -10
     return res
 
 
+def scale_grads(g: torch.Tensor, grad_h: Optional[torch.Tensor], grad_W: Optional[torch.Tensor],
+                w_dtype: torch.dtype):
+    """``flce_scale_grads``: returns (grad_h * g, grad_W * g in ``w_dtype``) as
+    new tensors (None where the input is None), g an fp32 scalar that stays on
+    the device; one read and one write of each gradient."""
+    dev = g.device
+    g32 = g.detach().reshape(1).to(torch.float32).contiguous()
+    gh_out = torch.empty_like(grad_h) if grad_h is not None else None
+    gW_out = torch.empty(grad_W.shape, dtype=w_dtype, device=dev) if grad_W is not None else None
+    n_h = grad_h.numel() if grad_h is not None else 0
+    n_W = grad_W.numel() if grad_W is not None else 0
+    rc = _lib.flce_scale_grads(_ptr(g32), _ptr(grad_h) if n_h else None, _ptr(gh_out) if n_h else None, n_h,
+                               _DTYPES[grad_h.dtype] if grad_h is not None else _lib.FLCE_DTYPE_F32,
+                               _ptr(grad_W) if n_W else None, _ptr(gW_out) if n_W else None, n_W,
+                               _DTYPES[w_dtype], torch.cuda.current_stream(dev).cuda_stream)
+    if rc != _lib.FLCE_OK:
+        raise _lib.FlceError(rc, "flce_scale_grads")
+    return gh_out, gW_out
+
+
 class _LinearCrossEntropy(torch.autograd.Function):
-    """mean / sum: the gradients come out of the fused forward call and are
-    scaled by the upstream scalar in backward.  none: the forward computes the
-    row losses only; backward recomputes the logits with the upstream row
-    gradients (grad_W mixes rows, so it cannot be rescaled afterwards)."""
+    """mean / sum: the gradients come out of the fused forward call; backward
+    scales them by the upstream scalar on the device (``flce_scale_grads``).
+    none: the forward computes the row losses only; backward recomputes the
+    logits with the upstream row gradients (grad_W mixes rows, so it cannot be
+    rescaled afterwards).  When neither h nor W needs a gradient the forward
+    is ``flce_fwd`` (no gradient GEMMs, no [V, H] accumulator).  Nothing here
+    synchronises unless ``check`` is set."""
 
     @staticmethod
-    def forward(ctx, h, W, labels, ignore_index, softcap, multiplier, reduction):
+    def forward(ctx, h, W, labels, ignore_index, softcap, multiplier, reduction, workspace, check):
         ctx.w_dtype = W.dtype
         ctx.reduction = reduction
-        if reduction == "none":
-            o = forward(h.detach(), W.detach(), labels, ignore_index, softcap, multiplier, "none")
-            ctx.save_for_backward(h.detach(), W.detach(), labels)
-            ctx.args = (ignore_index, softcap, multiplier)
-            return o.loss_rows.reshape(labels.shape), o.n_correct
-        o = fwd_bwd(h.detach(), W.detach(), labels, ignore_index, softcap, multiplier, reduction)
+        ctx.h_shape = h.shape
+        need = ctx.needs_input_grad[:2]
+        if reduction == "none" or not any(need):
+            o = forward(h.detach(), W.detach(), labels, ignore_index, softcap, multiplier, reduction,
+                        workspace=workspace, check=check)
+            if reduction == "none" and any(need):
+                ctx.save_for_backward(h.detach(), W.detach(), labels)
+                ctx.args = (ignore_index, softcap, multiplier, workspace)
+            loss = o.loss_rows if reduction == "none" else o.loss
+            return loss, o.n_correct
+        o = fwd_bwd(h.detach(), W.detach(), labels, ignore_index, softcap, multiplier, reduction,
+                    workspace=workspace, check=check)
         ctx.save_for_backward(o.grad_h, o.grad_W)
         return o.loss, o.n_correct
 
     @staticmethod
     def backward(ctx, grad_loss, _grad_n_correct):
+        need_h, need_W = ctx.needs_input_grad[:2]
         if ctx.reduction == "none":
             h, W, labels = ctx.saved_tensors
-            ignore_index, softcap, multiplier = ctx.args
-            o = fwd_bwd(h, W, labels, ignore_index, softcap, multiplier, "none",
-                        grad_rows=grad_loss.reshape(-1))
-            return o.grad_h, o.grad_W.to(ctx.w_dtype), None, None, None, None, None
+            ignore_index, softcap, multiplier, workspace = ctx.args
+            o = fwd_bwd(h, W, labels, ignore_index, softcap, multiplier, "none", workspace=workspace,
+                        check=False, grad_rows=grad_loss.reshape(-1))
+            gW = o.grad_W.to(ctx.w_dtype) if need_W else None
+            return (o.grad_h if need_h else None), gW, None, None, None, None, None, None, None
         gh, gW = ctx.saved_tensors
-        g = grad_loss.to(torch.float32)
-        gh = gh * g.to(gh.dtype)
-        gW = (gW * g).to(ctx.w_dtype)
-        return gh, gW, None, None, None, None, None
+        gh_out, gW_out = scale_grads(grad_loss, gh if need_h else None, gW if need_W else None, ctx.w_dtype)
+        return gh_out, gW_out, None, None, None, None, None, None, None
 
 
 def linear_cross_entropy(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
                          ignore_index: int = -100, softcap: Optional[float] = None,
-                         multiplier: float = 1.0, reduction: str = "mean"):
+                         multiplier: float = 1.0, reduction: str = "mean",
+                         workspace: Optional[torch.Tensor] = None, check: bool = False):
     """Differentiable FLCE: returns (loss, n_correct); token accuracy is
     n_correct / number of non-ignored labels (Muse Glimmer page, Summary
-    item 2).  With reduction "none" the loss has the shape of ``labels``."""
-    return _LinearCrossEntropy.apply(h, W, labels, ignore_index, softcap, multiplier, reduction)
+    item 2).  With reduction "none" the loss has the shape of ``labels``.
+
+    Nothing synchronises the host by default: out-of-range labels are
+    reported by ``read_status(workspace)`` on a caller-owned ``workspace``
+    (uint8, reused across steps), or at once with ``check=True``."""
+    return _LinearCrossEntropy.apply(h, W, labels, ignore_index, softcap, multiplier, reduction, workspace, check)

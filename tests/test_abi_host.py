@@ -189,6 +189,8 @@ def _call(**kw):
     (dict(softcap_T=float("nan")), L.FLCE_EINVAL),
     (dict(softcap_T=float("inf")), L.FLCE_EINVAL),
     (dict(multiplier=float("inf")), L.FLCE_EINVAL),
+    (dict(softcap_T=1e-39), L.FLCE_EINVAL),               # 1 / T overflows
+    (dict(softcap_T=1e-30, multiplier=1e10), L.FLCE_EINVAL),   # m / T overflows
     (dict(H=12), L.FLCE_EUNSUPPORTED),
     (dict(), L.FLCE_EWORKSPACE),
 ])
@@ -221,13 +223,17 @@ def _call_ex(opts, **kw):
     (_opts(loss_rows=66), dict(reduction=2), L.FLCE_EINVAL),         # misaligned
     (_opts(pred_rows=68), {}, L.FLCE_EINVAL),
     (_opts(loss_rows=64, grad_rows=66), dict(reduction=2), L.FLCE_EINVAL),
-    (_opts(grad_scale=float("nan")), {}, L.FLCE_EINVAL),
-    (_opts(grad_scale=float("inf")), {}, L.FLCE_EINVAL),
+    (_opts(grad_scale=float("nan"), use_grad_scale=1), {}, L.FLCE_EINVAL),
+    (_opts(grad_scale=float("inf"), use_grad_scale=1), {}, L.FLCE_EINVAL),
+    (_opts(use_grad_scale=2), {}, L.FLCE_EINVAL),
     (_opts(accumulate_grad_W=2), {}, L.FLCE_EINVAL),
     (None, dict(grad_W=None), L.FLCE_EINVAL),
     (None, {}, L.FLCE_EWORKSPACE),
-    (_opts(loss_rows=64, lse_rows=64, pred_rows=64, grad_rows=64, grad_scale=2.0, accumulate_grad_W=1),
-     dict(reduction=2), L.FLCE_EWORKSPACE),
+    # a scale that is not in use is not looked at
+    (_opts(grad_scale=float("nan")), {}, L.FLCE_EWORKSPACE),
+    (_opts(grad_scale=0.0, use_grad_scale=1), {}, L.FLCE_EWORKSPACE),
+    (_opts(loss_rows=64, lse_rows=64, pred_rows=64, grad_rows=64, grad_scale=2.0, accumulate_grad_W=1,
+           use_grad_scale=1), dict(reduction=2), L.FLCE_EWORKSPACE),
 ])
 def test_fwd_bwd_ex_rejects_before_launch(opts, kw, code):
     # fake addresses and a 64-byte workspace: nothing can reach a launch
@@ -324,8 +330,10 @@ def _call_ce(opts=None, **kw):
     (None, dict(grad_logits=512, ld_grad=12), L.FLCE_EINVAL),
     (None, dict(grad_logits=256, ld_grad=16, ld_logits=8), L.FLCE_EINVAL),   # in place needs equal ld
     (_opts(grad_rows=64), {}, L.FLCE_EINVAL),
-    (_opts(grad_scale=float("inf")), {}, L.FLCE_EINVAL),
+    (_opts(grad_scale=float("inf"), use_grad_scale=1), {}, L.FLCE_EINVAL),
+    (_opts(use_grad_scale=3), {}, L.FLCE_EINVAL),
     (None, {}, L.FLCE_EWORKSPACE),
+    (_opts(grad_scale=float("inf")), {}, L.FLCE_EWORKSPACE),   # not in use: not looked at
     (_opts(loss_rows=64, grad_rows=64), dict(reduction=2, grad_logits=256), L.FLCE_EWORKSPACE),
 ])
 def test_cross_entropy_rejects_before_launch(opts, kw, code):
@@ -357,3 +365,41 @@ def test_one_hip_runtime_whatever_the_import_order():
     assert out.returncode == 0, out.stderr[-2000:]
     maps = eval(out.stdout.strip().splitlines()[-1])
     assert len(maps) == 1, maps
+
+
+def _call_scale(**kw):
+    args = dict(grad_scale=4, grad_h_in=16, grad_h_out=16, n_h=8, h_dtype=0, grad_W_in=1 << 20,
+                grad_W_out=2 << 20, n_W=8, w_dtype=0, stream=0)
+    args.update(kw)
+    return L.flce_scale_grads(*args.values())
+
+
+@pytest.mark.parametrize("kw", [
+    dict(grad_scale=None), dict(grad_scale=6),                 # null / misaligned scale
+    dict(n_h=-1), dict(n_W=-1), dict(h_dtype=2), dict(w_dtype=5),
+    dict(grad_h_in=None), dict(grad_h_out=24), dict(grad_W_in=None), dict(grad_W_out=(2 << 20) + 8),
+    dict(grad_h_out=32, n_h=16),                                  # partly overlaps grad_h_in (16 bytes in)
+    dict(grad_W_out=(1 << 20) + 16),                              # bf16 out inside the fp32 input
+    dict(grad_W_out=1 << 20),                                     # bf16 out over its own fp32 input
+    dict(grad_W_out=(1 << 20) + 16, w_dtype=1),                   # fp32: only exactly in place
+])
+def test_scale_grads_rejects_before_launch(kw):
+    """flce_scale_grads checks its pointers, sizes, dtypes and overlaps on the
+    host.  The addresses are fake and the call has no workspace to fail on, so
+    a check that let one through would launch: CPU hosts only."""
+    from conftest import gpu_available
+    if gpu_available():
+        pytest.skip("fake device addresses: run on a host without a GPU")
+    assert _call_scale(**kw) == L.FLCE_EINVAL
+
+
+def test_plan_budget_shrinks_the_split_before_the_chunk():
+    """Under a budget that binds, the planner first gives up grad_h splits
+    (their fp32 partials) and only then chunk rows."""
+    N, H, V = 4096, 4096, 128256
+    assert L.flce_plan(N, H, V, 0).split_k == 2
+    a = L.flce_plan(N, H, V, 0, 300 << 20)
+    assert (a.chunk_rows, a.split_k) == (768, 6) and a.workspace_bytes <= 300 << 20
+    b = L.flce_plan(N, H, V, 0, a.workspace_bytes - 1)
+    assert b.chunk_rows == a.chunk_rows and b.split_k < a.split_k
+    assert b.workspace_bytes <= a.workspace_bytes - 1

@@ -121,3 +121,39 @@ def test_cross_entropy_reduction_none_row_gradients():
     e_r = float(np.max(np.abs(o.loss_rows.cpu().numpy() - ref["loss_rows"]) / np.maximum(np.abs(ref["loss_rows"]), 1)))
     log(f"[logits] none: rows {e_r:.2e} grad {e_g:.2e}")
     assert e_r <= 1e-5 and e_g <= 1e-2
+
+
+@pytest.mark.parametrize("m,T", [(0.5, 30.0), (-0.37, 1.0), (1.0, 2.0), (1.0, 1.5e-5), (0.5, 0.0)])
+def test_softcap_on_the_gpu_matches_float64_tanh(m, T):
+    """The kernels' softcap (Muse Glimmer page, Details > Softcap) on chosen raw
+    logits: fp32 h rows [x, 0, 0, 0] against W rows [2^k, 0, 0, 0] make every
+    raw logit exactly x 2^k, so flce_logits returns T tanh(m x 2^k / T) as the
+    hardware computes it (exp2 and reciprocal instructions included).  Against
+    float64 tanh on the same float32 inputs: relative error <= 1e-6 over
+    |m a / T| from 1e-7 to 20, across the switch between the series and the
+    exponential form, for both signs (host bound 4e-7, tests/test_softcap_host.py,
+    plus the hardware approximations); exact zero at 0."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    dev = torch.device("cuda", 0)
+    s = abs(np.float32(m) / np.float32(T)) if T > 0 else abs(np.float32(m))
+    x = np.concatenate([np.linspace(0.0, 20.0, 3001), np.logspace(-7, 1.3, 1000), [0.25]])
+    x = np.concatenate([x, -x])
+    base_a = (x / s).astype(np.float32)
+    ks = np.arange(-2, 6)                     # W rows 2^k: the raw logit is x * 2^k / s exactly
+    h = np.zeros((base_a.size, 4), np.float32)
+    h[:, 0] = base_a
+    Wm = np.zeros((ks.size, 4), np.float32)
+    Wm[:, 0] = np.exp2(ks).astype(np.float32)
+    z = L.logits(torch.from_numpy(h).to(dev), torch.from_numpy(Wm).to(dev), T if T > 0 else None, m)
+    torch.cuda.synchronize()
+    z = z.cpu().numpy().astype(np.float64)
+    a = base_a.astype(np.float64)[:, None] * np.exp2(ks)[None, :]
+    m64, T64 = float(np.float32(m)), float(np.float32(T))
+    ref = T64 * np.tanh(m64 * a / T64) if T > 0 else m64 * a
+    nz = ref != 0.0
+    rel = np.abs(z[nz] - ref[nz]) / np.abs(ref[nz])
+    log(f"[softcap] m={m} T={T}: max rel {rel.max():.2e} over {nz.sum()} logits")
+    assert np.all(np.isfinite(z))
+    assert np.all(z[~nz] == 0.0)
+    assert rel.max() <= (1e-6 if T > 0 else 0.0)

@@ -204,3 +204,168 @@ def test_reused_outputs_gain_row_statistics():
     torch.cuda.synchronize()
     ref = oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, IGN, 1.0, 0.37, "mean")
     check_rows(case, ref, o.loss_rows, o.lse_rows, o.pred_rows)
+
+
+@pytest.mark.parametrize("red", ["mean", "none"])
+def test_batch_by_sequence_inputs_keep_their_shape(red):
+    """[B, S, H] hidden states and [B, S] labels are flattened to rows and the
+    outputs restored to the caller's shapes (SpecForge page, Changes): grad_h
+    as [B, S, H], per-row losses as [B, S]; every value bitwise equal to the
+    call on the flattened rows."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c4", 600, 256, 1000, 2.0, 0.5, "mean")
+    log(f"[options] [B, S, H] inputs, reduction {red}")
+    h, W, lab = to_device(case)
+    h3, l3 = h.reshape(3, 200, 256), lab.reshape(3, 200)
+    flat = L.fwd_bwd(h, W, lab, IGN, 2.0, 0.5, red)
+    shaped = L.fwd_bwd(h3, W, l3, IGN, 2.0, 0.5, red)
+    torch.cuda.synchronize()
+    assert shaped.grad_h.shape == (3, 200, 256)
+    assert torch.equal(shaped.grad_h.reshape(600, 256), flat.grad_h)
+    assert torch.equal(shaped.grad_W, flat.grad_W)
+    assert shaped.loss.item() == flat.loss.item() and shaped.n_correct.item() == flat.n_correct.item()
+    f3 = L.forward(h3, W, l3, IGN, 2.0, 0.5, red)
+    f1 = L.forward(h, W, lab, IGN, 2.0, 0.5, red)
+    torch.cuda.synchronize()
+    assert f3.loss.item() == f1.loss.item()
+    if red == "none":
+        assert shaped.loss_rows.shape == (3, 200) and f3.loss_rows.shape == (3, 200)
+        assert torch.equal(shaped.loss_rows.reshape(-1), flat.loss_rows)
+        assert torch.equal(f3.loss_rows.reshape(-1), f1.loss_rows)
+    # the differentiable wrapper: gradients arrive in the inputs' shapes
+    hh = h3.clone().requires_grad_(True)
+    WW = W.clone().requires_grad_(True)
+    loss, _ = L.linear_cross_entropy(hh, WW, l3, IGN, 2.0, 0.5, red)
+    (loss.sum() if red == "none" else loss).backward()
+    torch.cuda.synchronize()
+    assert hh.grad.shape == (3, 200, 256) and WW.grad.shape == W.shape and WW.grad.dtype == W.dtype
+    assert torch.equal(hh.grad.reshape(600, 256), flat.grad_h)
+    ref = oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, IGN, 2.0, 0.5, red)
+    _, gt = tolerances(case.cfg.dtype)
+    assert rel_fro(WW.grad.float().cpu().numpy(), ref["grad_W"]) <= gt
+
+
+def test_autograd_step_never_synchronises(monkeypatch):
+    """The differentiable wrapper enqueues its forward, backward and gradient
+    scaling without waiting for the device: the status reader (the library's
+    one synchronising call) must not run.  The upstream gradient stays on the
+    device and is applied in fp32 by flce_scale_grads; W's gradient comes back
+    in W's dtype."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    from linear_cross_entropy_gemm_amd import torch_api
+
+    def no_sync(*a, **k):
+        raise AssertionError("flce_read_status called in the training step")
+
+    case = make("c2", 600, 320, 1000, 1.0, 0.37, "mean")
+    log("[options] autograd step without synchronisation")
+    h, W, lab = to_device(case)
+    monkeypatch.setattr(torch_api._lib, "flce_read_status", no_sync)
+    hh = h.clone().requires_grad_(True)
+    WW = W.clone().requires_grad_(True)
+    g = torch.tensor(-1.7303, device=h.device)   # not representable in bf16
+    loss, nc = L.linear_cross_entropy(hh, WW, lab, IGN, 1.0, 0.37)
+    (loss * g).backward()
+    monkeypatch.undo()
+    torch.cuda.synchronize()
+    ref = oracle.flce_reference(case.h_f32(), case.W_f32(), case.labels, IGN, 1.0, 0.37, "mean",
+                                grad_scale=float(g.item()))
+    lt, gt = tolerances(case.cfg.dtype)
+    e_gh = rel_fro(hh.grad.float().cpu().numpy(), ref["grad_h"])
+    e_gW = rel_fro(WW.grad.float().cpu().numpy(), ref["grad_W"])
+    log(f"  grad_h {e_gh:.2e} grad_W {e_gW:.2e}")
+    assert abs(loss.item() - ref["loss"]) / ref["loss"] <= lt
+    assert e_gh <= gt and e_gW <= gt
+    assert WW.grad.dtype == torch.bfloat16 and hh.grad.dtype == torch.bfloat16
+
+
+def test_autograd_without_gradients_runs_forward_only():
+    """With no input needing a gradient the wrapper runs flce_fwd: the same
+    loss and n_correct bitwise, and no [V, H] accumulator."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c4", 513, 448, 2100, 30.0, 0.5, "mean")
+    h, W, lab = to_device(case)
+    full = L.fwd_bwd(h, W, lab, IGN, 30.0, 0.5)
+    with torch.no_grad():
+        loss, nc = L.linear_cross_entropy(h, W, lab, IGN, 30.0, 0.5)
+    torch.cuda.synchronize()
+    assert loss.item() == full.loss.item() and nc.item() == full.n_correct.item()
+    assert not loss.requires_grad
+
+
+def test_scale_grads_matches_torch():
+    """flce_scale_grads against plain torch on the same stored gradients:
+    fp32 products, one rounding to the output dtype (bitwise), in place and
+    out of place, with ragged element counts."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    dev = torch.device("cuda", 0)
+    rng = np.random.default_rng(5)
+    for n_h, n_W in [(1003, 4099), (8, 16), (0, 77), (129, 0)]:
+        gh = torch.from_numpy(rng.normal(size=n_h).astype(np.float32)).to(dev).bfloat16()
+        gW = torch.from_numpy(rng.normal(size=n_W).astype(np.float32)).to(dev)
+        for gv in (-1.7303, 1.0, 0.0, 3.0e-3):
+            g = torch.tensor(gv, device=dev)
+            oh, oW = L.scale_grads(g, gh if n_h else None, gW if n_W else None, torch.bfloat16)
+            torch.cuda.synchronize()
+            if n_h:
+                assert torch.equal(oh, (gh.float() * g).bfloat16())
+            if n_W:
+                assert torch.equal(oW, (gW * g).bfloat16())
+                _, o32 = L.scale_grads(g, None, gW, torch.float32)
+                assert torch.equal(o32, gW * g)
+        # in place (the raw call): grad_h_out = grad_h_in
+        x = gh.clone()
+        g = torch.tensor([0.5], device=dev)
+        rc = L.flce_scale_grads(g.data_ptr(), x.data_ptr() if n_h else None, x.data_ptr() if n_h else None, n_h,
+                                L.FLCE_DTYPE_BF16, None, None, 0, L.FLCE_DTYPE_F32,
+                                torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert rc == L.FLCE_OK
+        assert torch.equal(x, (gh.float() * 0.5).bfloat16())
+
+
+def test_zero_upstream_gradient_gives_zero_gradients():
+    """grad_scale = 0 is an upstream gradient of zero: grad_h and this call's
+    grad_W term are zero (accumulation leaves grad_W as it was)."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c2", 600, 320, 1000, 1.0, 0.37, "mean")
+    h, W, lab = to_device(case)
+    o = L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, grad_scale=0.0)
+    torch.cuda.synchronize()
+    assert o.grad_h.abs().max().item() == 0.0 and o.grad_W.abs().max().item() == 0.0
+    before = torch.randn_like(o.grad_W)
+    o.grad_W.copy_(before)
+    L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, out=o, accumulate_grad_W=True, grad_scale=0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o.grad_W, before)
+
+
+def test_reused_outputs_of_another_call_are_rejected():
+    """An output set whose buffers do not match the call (a smaller N, V or H,
+    grad_W in bf16, a strided view) is rejected before anything is enqueued,
+    and the buffers stay as they were."""
+    import torch
+    import linear_cross_entropy_gemm_amd as L
+    case = make("c2", 600, 320, 1000, 1.0, 0.37, "mean")
+    h, W, lab = to_device(case)
+    o = L.fwd_bwd(h[:300], W[:500], lab[:300].clamp(max=499), IGN, 1.0, 0.37)
+    torch.cuda.synchronize()
+    snap = (o.grad_h.clone(), o.grad_W.clone())
+    with pytest.raises(ValueError):
+        L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, out=o)                       # larger N and V
+    o2 = L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37)
+    bad = [dict(grad_W=o2.grad_W.bfloat16()), dict(grad_W=o2.grad_W.t()), dict(grad_h=o2.grad_h[:, :160]),
+           dict(n_correct=o2.n_correct.float()), dict(loss=o2.loss.reshape(1))]
+    for kw in bad:
+        import dataclasses
+        with pytest.raises(ValueError):
+            L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, out=dataclasses.replace(o2, **kw))
+    torch.cuda.synchronize()
+    assert torch.equal(o.grad_h, snap[0]) and torch.equal(o.grad_W, snap[1])
+    with pytest.raises(ValueError):
+        L.fwd_bwd(h, W, lab, IGN, 1.0, 0.37, workspace=torch.empty(16, dtype=torch.uint8, device=h.device))
