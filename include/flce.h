@@ -63,7 +63,8 @@ enum {
   FLCE_EWORKSPACE = 2,    /* workspace smaller than flce_workspace_size() for the call */
   FLCE_EDEVICE = 3,       /* a HIP launch or runtime call failed */
   FLCE_ELABEL = 4,        /* (device-detected) a label outside [0, V) that is not ignore_index */
-  FLCE_EUNSUPPORTED = 5   /* valid but unsupported shape, e.g. H not a multiple of 8 (bf16) / 4 (fp32) or too large */
+  FLCE_EUNSUPPORTED = 5,  /* valid but unsupported shape, e.g. H not a multiple of 8 (bf16) / 4 (fp32) or too large */
+  FLCE_ESCRATCH = 6       /* flce_fwd_bwd_noalloc: no chunk plan fits its static scratch (FLCE_NOALLOC_SCRATCH_BYTES) */
 };
 
 /*
@@ -193,6 +194,34 @@ int flce_fwd_bwd_ex(const void* h, const void* W, const int64_t* labels,
                     float* loss, void* grad_h, float* grad_W, int64_t* n_correct,
                     hipStream_t stream, int dtype, void* workspace, size_t workspace_bytes,
                     const flce_options_t* options);
+
+/*
+ * flce_fwd_bwd_ex for callers that cannot allocate device memory: code under
+ * HIP graph (stream) capture, tight training or serving loops, harnesses that
+ * forbid allocation.  Same arguments, formulas, options and errors as
+ * flce_fwd_bwd_ex except:
+ *   - no workspace argument: the scratch is a static device array of
+ *     FLCE_NOALLOC_SCRATCH_BYTES that each GPU running the library holds from
+ *     the first call there until the process ends; the chunk plan is the
+ *     largest that fits it (flce_plan with that budget), and sizes for which
+ *     none fits return FLCE_ESCRATCH before anything is enqueued;
+ *   - status  [1] int32 device pointer (4-byte aligned) or NULL: receives, in
+ *     the call's last kernel, FLCE_OK or FLCE_ELABEL (the device-side label
+ *     check that flce_read_status reports for the other entry points).
+ * Nothing is allocated (no hipMalloc, no library allocation) and nothing
+ * synchronises.  All calls on one GPU share its scratch and each call
+ * overwrites it, so calls that overlap in time on the same GPU (different
+ * streams without ordering, or different threads) race and give wrong
+ * results: order them.  The first call on each device looks up the scratch's
+ * device address (hipGetSymbolAddress) with that device current; the call
+ * uses the current device, which must be the device of `stream`.
+ */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int flce_fwd_bwd_noalloc(const void* h, const void* W, const int64_t* labels,
+                         int64_t N, int64_t H, int64_t V,
+                         int64_t ignore_index, float softcap_T, float multiplier, int reduction,
+                         float* loss, void* grad_h, float* grad_W, int64_t* n_correct, int* status,
+                         hipStream_t stream, int dtype, const flce_options_t* options);
 
 /*
  * Workspace bytes needed by flce_fwd (forward only: no logits transient and

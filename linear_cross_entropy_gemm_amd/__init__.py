@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     FLCE_EDEVICE,
     FLCE_EINVAL,
     FLCE_ELABEL,
+    FLCE_ESCRATCH,
     FLCE_EUNSUPPORTED,
     FLCE_EWORKSPACE,
     FLCE_OK,
@@ -23,12 +24,14 @@ from ._lib import (  # noqa: F401
     FLCE_REDUCTION_NONE,
     FLCE_REDUCTION_SUM,
     KERNEL_KINDS,
+    NOALLOC_SCRATCH_BYTES,
     FlceError,
     flce_cross_entropy,
     flce_cross_entropy_workspace_size,
     flce_fwd,
     flce_fwd_bwd,
     flce_fwd_bwd_ex,
+    flce_fwd_bwd_noalloc,
     flce_fwd_workspace_size,
     flce_logits,
     flce_options_t,

@@ -25,9 +25,14 @@ FLCE_EWORKSPACE = 2
 FLCE_EDEVICE = 3
 FLCE_ELABEL = 4
 FLCE_EUNSUPPORTED = 5
+FLCE_ESCRATCH = 6
+
+# Static scratch of flce_fwd_bwd_noalloc (FLCE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 # Every symbol include/flce.h declares.
-EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_fwd_bwd_ex", "flce_fwd_workspace_size",
+EXPORTED = ("flce_plan", "flce_workspace_size", "flce_fwd_bwd", "flce_fwd_bwd_ex", "flce_fwd_bwd_noalloc",
+            "flce_fwd_workspace_size",
             "flce_fwd", "flce_logits", "flce_cross_entropy_workspace_size", "flce_cross_entropy",
             "flce_scale_grads", "flce_read_status", "flce_strerror", "flce_profile_enable", "flce_profile_read")
 
@@ -97,6 +102,9 @@ def _load() -> ctypes.CDLL:
     lib.flce_fwd_bwd_ex.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
                                     vp, vp, vp, vp, vp, i32, vp, sz, ctypes.POINTER(flce_options_t)]
     lib.flce_fwd_bwd_ex.restype = i32
+    lib.flce_fwd_bwd_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
+                                         vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(flce_options_t)]
+    lib.flce_fwd_bwd_noalloc.restype = i32
     lib.flce_fwd_workspace_size.argtypes = [i64, i64, i64, i32, sz]
     lib.flce_fwd_workspace_size.restype = sz
     lib.flce_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, f32, i32,
@@ -159,6 +167,17 @@ def flce_fwd_bwd_ex(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_
     return int(_lib.flce_fwd_bwd_ex(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier,
                                     reduction, loss, grad_h, grad_W, n_correct, stream, dtype,
                                     workspace, workspace_bytes, _opts(options)))
+
+
+def flce_fwd_bwd_noalloc(h: int, W: int, labels: int, N: int, H: int, V: int, ignore_index: int,
+                         softcap_T: float, multiplier: float, reduction: int, loss: int, grad_h: int,
+                         grad_W: int, n_correct, status, stream: int, dtype: int, options) -> int:
+    """Raw call of the allocation-free variant (static scratch, no workspace
+    argument; ``status`` receives the device-side status word).  Returns the
+    C return code."""
+    return int(_lib.flce_fwd_bwd_noalloc(h, W, labels, N, H, V, ignore_index, softcap_T, multiplier,
+                                         reduction, loss, grad_h, grad_W, n_correct, status, stream, dtype,
+                                         _opts(options)))
 
 
 def flce_fwd_workspace_size(N: int, H: int, V: int, dtype: int, budget_bytes: int = 0) -> int:

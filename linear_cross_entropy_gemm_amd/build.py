@@ -15,8 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflce.so")
 
-SOURCES = ["flce_kernels.hip", "flce_logits.hip", "flce_scale.hip", "flce_plan.cpp", "flce_api.cpp",
-           "flce_profile.cpp"]
+SOURCES = ["flce_kernels.hip", "flce_logits.hip", "flce_scale.hip", "flce_noalloc.hip", "flce_plan.cpp",
+           "flce_api.cpp", "flce_profile.cpp"]
 HEADERS = ["device_common.hpp", "gemm_tile.hpp", "flce_internal.hpp", "kernel_args.hpp"]
 
 ARCH = "gfx950"

@@ -95,6 +95,7 @@ static __global__ __launch_bounds__(1024) void finalize_kernel(FinalizeArgs p) {
     const double s = (p.reduction == FLCE_REDUCTION_MEAN) ? (nv ? 1.0 / (double)nv : 0.0) : 1.0;
     *p.loss = (float)(s * ls[0]);
     if (p.n_correct) *p.n_correct = cs[0];
+    if (p.status_out) *p.status_out = p.hdr->status;
   }
 }
 

@@ -279,6 +279,7 @@ extern "C" const char* flce_strerror(int code) {
     case FLCE_EDEVICE: return "HIP launch or runtime call failed";
     case FLCE_ELABEL: return "a label outside [0, V) that is not ignore_index";
     case FLCE_EUNSUPPORTED: return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32; H <= 2^21; V <= 2^22 - 256 for bf16, 2^21 - 256 for fp32)";
+    case FLCE_ESCRATCH: return "no chunk plan fits the 256 MiB static scratch of flce_fwd_bwd_noalloc (use flce_fwd_bwd_ex with a workspace)";
     default: return "unknown error code";
   }
 }

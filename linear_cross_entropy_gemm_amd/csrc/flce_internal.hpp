@@ -63,6 +63,8 @@ struct CallArgs {
   float grad_scale = 1.0f;
   bool accumulate_grad_W = false;
   bool fwd_only = false;
+  int* status_out = nullptr;   // device copy of the final status word (null: none)
+  bool profile = true;         // false: no timing events even when profiling is on
 };
 
 // Enqueue the whole call on `stream`.  Returns FLCE_OK or FLCE_EDEVICE.
@@ -111,7 +113,8 @@ struct CeCallArgs {
 int run_cross_entropy(const CeCallArgs& a, hipStream_t stream);
 size_t cross_entropy_workspace(int64_t N);
 
-// Brackets one kernel launch with timing events when profiling is enabled.
+// Brackets one kernel launch with timing events when profiling is enabled
+// (kind < 0: never).
 class ProfileScope {
  public:
   ProfileScope(int kind, hipStream_t st);

@@ -656,7 +656,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   const float capT = a.softcap_T > 0.0f ? a.softcap_T : 0.0f;
 
   {
-    ProfileScope ps(FLCE_KERNEL_LABEL_SCAN, st);
+    ProfileScope ps(a.profile ? FLCE_KERNEL_LABEL_SCAN : -1, st);
     header_init_kernel<<<1, 64, 0, st>>>(hdr);
     if (pack) {
       const int64_t nb = (a.N + kPackRows - 1) / kPackRows;
@@ -673,7 +673,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     }
   }
   if (pl.n_chunks == 0 && !a.fwd_only && !a.accumulate_grad_W) {
-    ProfileScope ps(FLCE_KERNEL_ZERO, st);
+    ProfileScope ps(a.profile ? FLCE_KERNEL_ZERO : -1, st);
     const int64_t n = a.V * a.H;
     const unsigned g = grid_1d(n, 256);
     zero_f32_kernel<<<g < 65536 ? g : 65536, 256, 0, st>>>(a.grad_W, n);
@@ -700,7 +700,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     f.map = TileMap{tiles_voc, tiles_tok, 1, 4, 1, 0};
     f.packed = packed; f.c0 = c0;
     {
-      ProfileScope ps(FLCE_KERNEL_FWD_LOGITS, st);
+      ProfileScope ps(a.profile ? FLCE_KERNEL_FWD_LOGITS : -1, st);
       if (a.fwd_only)
         fwd_logits_kernel<T, false><<<tiles_voc * tiles_tok, kThreads, 0, st>>>(f);
       else
@@ -714,7 +714,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     m.C_this = Ct;
     m.packed = packed; m.c0 = c0;
     {
-      ProfileScope ps(FLCE_KERNEL_ROW_MERGE, st);
+      ProfileScope ps(a.profile ? FLCE_KERNEL_ROW_MERGE : -1, st);
       row_merge_kernel<<<grid_1d(Ct, 64), 1024, 0, st>>>(m);
     }
     if (a.fwd_only) continue;
@@ -727,7 +727,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gl.grad_rows = a.grad_rows ? (pack ? pgrow : a.grad_rows) + c0 : nullptr;
     gl.packed = packed; gl.c0 = c0;
     {
-      ProfileScope ps(FLCE_KERNEL_GRAD_LOGITS, st);
+      ProfileScope ps(a.profile ? FLCE_KERNEL_GRAD_LOGITS : -1, st);
       grad_logits_kernel<T><<<grid_1d((int64_t)Ct * (Vp / Elem<T>::per_chunk), 256), 256, 0, st>>>(gl);
     }
 
@@ -742,7 +742,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gh.map = TileMap{tiles_tok, tiles_hid, splits, tiles_tok, 0, 0};
     gh.packed = packed; gh.c0 = c0;
     {
-      ProfileScope ps(FLCE_KERNEL_GRAD_H, st);
+      ProfileScope ps(a.profile ? FLCE_KERNEL_GRAD_H : -1, st);
       grad_h_kernel<T><<<tiles_tok * tiles_hid * splits, kThreads, 0, st>>>(gh);
     }
 
@@ -753,7 +753,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gr.out = a.grad_h;
     gr.packed = packed; gr.c0 = c0; gr.prow = pack ? prow : nullptr;
     {
-      ProfileScope ps(FLCE_KERNEL_GRAD_H_REDUCE, st);
+      ProfileScope ps(a.profile ? FLCE_KERNEL_GRAD_H_REDUCE : -1, st);
       grad_h_reduce_kernel<T><<<grid_1d(gr.groups, 256), 256, 0, st>>>(gr);
     }
 
@@ -764,7 +764,7 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
     gw.map = TileMap{tiles_hid, tiles_voc, 1, 4, 1, 1};
     gw.packed = packed; gw.c0 = c0;
     {
-      ProfileScope ps(FLCE_KERNEL_GRAD_W, st);
+      ProfileScope ps(a.profile ? FLCE_KERNEL_GRAD_W : -1, st);
       if (gw.accumulate)
         grad_W_kernel<T, true><<<tiles_hid * tiles_voc, kThreads, 0, st>>>(gw);
       else
@@ -776,12 +776,13 @@ static int run_typed(const CallArgs& a, const Plan& pl, hipStream_t st) {
   fa.loss_row = loss_row; fa.lse = lse; fa.pred = pred; fa.hdr = hdr; fa.reduction = a.reduction;
   fa.loss = a.loss; fa.n_correct = a.n_correct;
   fa.loss_rows = a.loss_rows; fa.lse_rows = a.lse_rows; fa.pred_rows = a.pred_rows;
+  fa.status_out = a.status_out;
   if (pack) {
     fa.ppos = ppos;
     fa.plab = plab;
   }
   {
-    ProfileScope ps(FLCE_KERNEL_FINALIZE, st);
+    ProfileScope ps(a.profile ? FLCE_KERNEL_FINALIZE : -1, st);
     finalize_kernel<<<1, 1024, 0, st>>>(fa);
   }
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_EDEVICE;

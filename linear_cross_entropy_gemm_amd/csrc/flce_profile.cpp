@@ -48,7 +48,7 @@ bool profile_on() { return state().on; }
 
 ProfileScope::ProfileScope(int kind, hipStream_t st) : kind_(kind), st_(st) {
   State& s = state();
-  if (!s.on) return;
+  if (!s.on || kind < 0) return;
   std::lock_guard<std::mutex> g(s.mu);
   a_ = take_event(s);
   b_ = take_event(s);

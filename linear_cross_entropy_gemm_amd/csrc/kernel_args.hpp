@@ -125,6 +125,7 @@ struct FinalizeArgs {
   // holds the packed labels
   const int* ppos = nullptr;
   const int64_t* plab = nullptr;
+  int* status_out = nullptr;   // receives the header's final status word (null: none)
 };
 
 }  // namespace flce
