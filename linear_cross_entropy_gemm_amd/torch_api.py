@@ -90,8 +90,8 @@ def _check_out(out: "FlceOutputs", N: int, H: int, V: int, h_dtype, dev) -> None
             if name in ("loss", "grad_h", "grad_W", "n_correct"):
                 raise ValueError(f"out.{name} is missing")
             continue
-        if name == "grad_h":
-            ok_shape = t.numel() == N * H and (t.dim() == 0 or t.shape[-1] == H or N * H == 0)
+        if name == "grad_h":   # any shape of N x H elements with rows of H (restored to h's shape)
+            ok_shape = t.dim() >= 1 and t.numel() == N * H and t.shape[-1] == H
         else:
             ok_shape = tuple(t.shape) == shape
         if not ok_shape:
@@ -133,6 +133,9 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     if ws_bytes == 0:
         raise _lib.FlceError(_lib.FLCE_EUNSUPPORTED, "flce_workspace_size")
     dev = h.device
+    if workspace is None and out is not None and out.workspace is not None \
+            and out.workspace.device == dev and out.workspace.numel() >= ws_bytes:
+        workspace = out.workspace   # a reused output set brings its workspace along
     workspace = _workspace(workspace, ws_bytes, dev)
     if accumulate_grad_W and out is None:
         raise ValueError("accumulate_grad_W needs out.grad_W holding the running sum")

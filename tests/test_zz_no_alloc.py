@@ -142,3 +142,66 @@ def test_noalloc_reports_bad_labels_in_its_status_word():
     got = _noalloc_call(h, W, lab, 300, 256, 777, 1.0, 0.37, "mean", L.FLCE_DTYPE_BF16)
     assert got[4] == L.FLCE_OK
     torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+@pytest.mark.usefixtures("require_gpu")
+def test_noalloc_call_replays_from_a_captured_graph():
+    """The use the entry point is for: a call captured into a HIP graph (it
+    allocates nothing and records only kernels), replayed several times with
+    the program's own work and synchronisations in between; every replay
+    equals the eager call bitwise, and the inputs changed in place between
+    replays are picked up."""
+    import torch
+    case = _case("c4", 700, 256, 1100, 30.0, 0.5, "mean")
+    c = case.cfg
+    N, H, V = 700, 256, 1100
+    h, W, lab = to_device(case)
+    dev = h.device
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    gh = torch.empty((N, H), dtype=h.dtype, device=dev)
+    gW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    nc = torch.empty((), dtype=torch.int64, device=dev)
+    st = torch.full((1,), -1, dtype=torch.int32, device=dev)
+
+    def call():
+        rc = L.flce_fwd_bwd_noalloc(h.data_ptr(), W.data_ptr(), lab.data_ptr(), N, H, V, IGN, c.softcap_T,
+                                    c.multiplier, L.FLCE_REDUCTION_MEAN, loss.data_ptr(), gh.data_ptr(),
+                                    gW.data_ptr(), nc.data_ptr(), st.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream, L.FLCE_DTYPE_BF16, None)
+        assert rc == L.FLCE_OK
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        call()                      # eager: also looks up the scratch on this device
+    torch.cuda.synchronize()
+    eager = (loss.clone(), gh.clone(), gW.clone(), nc.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    h0 = h.clone()
+    for rep in range(4):
+        loss.zero_(); gh.zero_(); gW.zero_(); nc.zero_(); st.fill_(-1)
+        if rep == 3:
+            h.mul_(-1.0)            # new inputs in the captured buffers
+        graph.replay()
+        torch.cuda.synchronize()
+        if rep < 3:
+            want = eager
+        else:
+            call()                  # eager on the new inputs, for comparison
+            torch.cuda.synchronize()
+            want = (loss.clone(), gh.clone(), gW.clone(), nc.clone())
+            loss.zero_(); gh.zero_(); gW.zero_(); nc.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+        got = (loss, gh, gW, nc)
+        same = [torch.equal(x, y) for x, y in zip(got, want)]
+        log(f"[noalloc] graph replay {rep}: bitwise equal {same}, status {int(st.item())}")
+        assert all(same) and int(st.item()) == L.FLCE_OK
+        # the program's own work between replays
+        o = L.fwd_bwd(h, W, lab, IGN, c.softcap_T, c.multiplier, "mean")
+        torch.cuda.synchronize()
+        assert o.loss.item() == want[0].item()
+    h.copy_(h0)
