@@ -483,7 +483,9 @@ __global__ __launch_bounds__(kThreads, 1) void grad_W_kernel(GradWArgs p) {
     la.init(p.h, p.ldh, tm * kTile, p.H, Ct, 0, wm * 128, lane);
     lb.init(p.G, p.ldg, tn * kTile, p.Vp, Ct, 0, wn * 128, lane);
     constexpr int bk = kDKBytes / 2;
-    gemm_mainloop_direct(la, lb, (Ct + bk - 1) / bk, smem, acc);
+    // G (B) streams from memory, the chunk's h rows are mostly cached: G's
+    // loads go first in each step, which gives them two steps to land
+    gemm_mainloop_direct<true>(la, lb, (Ct + bk - 1) / bk, smem, acc);
   } else {
     MNMajorLoader<T> la, lb;
     la.init(p.h, p.ldh, tm * kTile, p.H, Ct, 0);

@@ -650,12 +650,15 @@ __device__ __forceinline__ void lds_barrier() {
 // the wave waits for A_{t+1} and B_{t+1} and for its own LDS reads, and the
 // barrier both publishes them and frees the slots of A_t and B_t; the last
 // sub-step then runs from registers while reading sub-step 0 of step t + 1
-// and issuing B_{t+2}.  The last two steps issue no loads (nothing past the
-// K extent is fetched) and wait for everything before their barriers.  The
-// products are added to the values `acc` holds on entry.  Ends with every
-// load landed and a barrier, after which the LDS may be reused by the
-// epilogue.
-template <class LA, class LB>
+// and issuing B_{t+2}.  So A's loads have about 1.75 steps to land and B's
+// one; the stream is latency-bound, so the operand that comes from farther
+// away (more misses in L2) should go first: kBFirst swaps the roles (B_{t+2}
+// at sub-step 0, A_{t+2} after the barrier).  The last two steps issue no
+// loads (nothing past the K extent is fetched) and wait for everything
+// before their barriers.  The products are added to the values `acc` holds
+// on entry.  Ends with every load landed and a barrier, after which the LDS
+// may be reused by the epilogue.
+template <bool kBFirst = false, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, char* smem, f32x16 (&acc)[4][4]) {
   if (nk <= 0) return;
   auto slot = [&](int q) -> char* { return smem + q * kDOperand; };
@@ -666,22 +669,30 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
     for (int j = 0; j < kDLoads; ++j) ld.issue_part(slot_lds(q), j);
     ld.advance();
   };
-  issue_all(la, 0);
-  issue_all(lb, 1);
-  issue_all(la, 2);
-  issue_all(lb, 3);
+  constexpr int kA0 = kBFirst ? 1 : 0, kB0 = kBFirst ? 0 : 1;
+  if constexpr (kBFirst) {
+    issue_all(lb, 0);
+    issue_all(la, 1);
+    issue_all(lb, 2);
+    issue_all(la, 3);
+  } else {
+    issue_all(la, 0);
+    issue_all(lb, 1);
+    issue_all(la, 2);
+    issue_all(lb, 3);
+  }
   FLCE_WAIT_VMCNT(2 * kDLoads);
   __syncthreads();
   u32x4 a[2][4], b[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    b[0][i] = lb.read(slot(1), i, 0);
-    a[0][i] = la.read(slot(0), i, 0);
+    b[0][i] = lb.read(slot(kB0), i, 0);
+    a[0][i] = la.read(slot(kA0), i, 0);
   }
-  int sa = 0, sb = 1, sfree = 4;   // slots of A_t, B_t and of B_{t-1} (free)
+  int sa = kA0, sb = kB0, sfree = 4;   // slots of A_t, B_t and the free one
   // One K step.  kAhead: step t + 2 exists and is loaded.  The last two steps
   // run without loads (nothing past the K extent is fetched), so there nothing
-  // newer than B_{t+1} is in flight when the step waits for it.
+  // newer than step t + 1 is in flight when the step waits for it.
   auto step = [&](auto ahead_tag) {
     constexpr bool kAhead = decltype(ahead_tag)::value;
     const int na = sa + 2 >= kDSlots ? sa + 2 - kDSlots : sa + 2;
@@ -714,19 +725,39 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
           a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
         }
         if constexpr (kAhead) {
-          if (ks == 0) {
-            la.issue_part(slot_lds(sfree), 2 * g);
-            la.issue_part(slot_lds(sfree), 2 * g + 1);
-          } else if (last) {
-            lb.issue_part(slot_lds(sa), 2 * g);
-            lb.issue_part(slot_lds(sa), 2 * g + 1);
+          if constexpr (kBFirst) {
+            if (ks == 0) {
+              lb.issue_part(slot_lds(sfree), 2 * g);
+              lb.issue_part(slot_lds(sfree), 2 * g + 1);
+            } else if (last) {
+              la.issue_part(slot_lds(sb), 2 * g);
+              la.issue_part(slot_lds(sb), 2 * g + 1);
+            }
+          } else {
+            if (ks == 0) {
+              la.issue_part(slot_lds(sfree), 2 * g);
+              la.issue_part(slot_lds(sfree), 2 * g + 1);
+            } else if (last) {
+              lb.issue_part(slot_lds(sa), 2 * g);
+              lb.issue_part(slot_lds(sa), 2 * g + 1);
+            }
           }
         }
       }
-      if (kAhead && ks == 0) la.advance();
+      if (kAhead && ks == 0) {
+        if constexpr (kBFirst)
+          lb.advance();
+        else
+          la.advance();
+      }
     }
-    if (kAhead) lb.advance();
-    sfree = sb;
+    if (kAhead) {
+      if constexpr (kBFirst)
+        la.advance();
+      else
+        lb.advance();
+    }
+    sfree = kBFirst ? sa : sb;
     sa = na;
     sb = nb;
   };
