@@ -466,7 +466,7 @@ constexpr int kDLoads = kDKBytes / 16;          // load instructions per wave pe
 constexpr int kDOperand = kTile * kDKBytes;     // one slot
 constexpr int kDLdsBytes = kDSlots * kDOperand;
 static_assert(kDLdsBytes <= 160 * 1024, "LDS capacity");
-static_assert(kDSub == 4 && kDLoads == 8, "the K loop issues two loads per MFMA group");
+static_assert(kDSub == 4 && kDLoads == 8, "the K loop issues one or two loads per MFMA group");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define FLCE_AS3 __attribute__((address_space(3)))
@@ -646,14 +646,14 @@ __device__ __forceinline__ void lds_barrier() {
 // K loop of the direct-to-LDS pipeline.  Per K step, four sub-steps of 16
 // MFMAs per wave, each split into 4 block-row groups fenced in program order;
 // alongside each group the next sub-step's fragments are read (B first).
-// Sub-step 0 issues A_{t+2} (two loads per group).  Before the last sub-step
+// Sub-steps 0 and 1 issue A_{t+2} (one load per group).  Before the last sub-step
 // the wave waits for A_{t+1} and B_{t+1} and for its own LDS reads, and the
 // barrier both publishes them and frees the slots of A_t and B_t; the last
 // sub-step then runs from registers while reading sub-step 0 of step t + 1
-// and issuing B_{t+2}.  So A's loads have about 1.75 steps to land and B's
+// and issuing B_{t+2}.  So A's loads have about 1.5 steps to land and B's
 // one; the stream is latency-bound, so the operand that comes from farther
 // away (more misses in L2) should go first: kBFirst swaps the roles (B_{t+2}
-// at sub-step 0, A_{t+2} after the barrier).  The last two steps issue no
+// during sub-steps 0 and 1, A_{t+2} after the barrier).  The last two steps issue no
 // loads (nothing past the K extent is fetched) and wait for everything
 // before their barriers.  The products are added to the values `acc` holds
 // on entry.  Ends with every load landed and a barrier, after which the LDS
@@ -725,18 +725,18 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
           a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
         }
         if constexpr (kAhead) {
+          // first operand: one load per group over sub-steps 0 and 1;
+          // second: two per group once the barrier has freed its slot
           if constexpr (kBFirst) {
-            if (ks == 0) {
-              lb.issue_part(slot_lds(sfree), 2 * g);
-              lb.issue_part(slot_lds(sfree), 2 * g + 1);
+            if (ks < 2) {
+              lb.issue_part(slot_lds(sfree), 4 * ks + g);
             } else if (last) {
               la.issue_part(slot_lds(sb), 2 * g);
               la.issue_part(slot_lds(sb), 2 * g + 1);
             }
           } else {
-            if (ks == 0) {
-              la.issue_part(slot_lds(sfree), 2 * g);
-              la.issue_part(slot_lds(sfree), 2 * g + 1);
+            if (ks < 2) {
+              la.issue_part(slot_lds(sfree), 4 * ks + g);
             } else if (last) {
               lb.issue_part(slot_lds(sa), 2 * g);
               lb.issue_part(slot_lds(sa), 2 * g + 1);
@@ -744,7 +744,7 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
           }
         }
       }
-      if (kAhead && ks == 0) {
+      if (kAhead && ks == 1) {
         if constexpr (kBFirst)
           lb.advance();
         else
