@@ -645,7 +645,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // K loop of the direct-to-LDS pipeline.  Per K step, four sub-steps of 16
 // MFMAs per wave, each split into 4 block-row groups fenced in program order;
-// alongside each group the next sub-step's fragments are read (B first).
+// a group issues its global loads first, then its MFMAs and reads of the
+// next sub-step's fragments (B first).
 // Sub-steps 0 and 1 issue A_{t+2} (one load per group).  Before the last sub-step
 // the wave waits for A_{t+1} and B_{t+1} and for its own LDS reads, and the
 // barrier both publishes them and frees the slots of A_t and B_t; the last
@@ -716,14 +717,6 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         FLCE_FENCE();
-        mma_row(acc, a[p][g], b[p], g, bf16{});
-        if (g < 2) {
-          b[q][2 * g] = lb.read(srcb, 2 * g, nks);
-          b[q][2 * g + 1] = lb.read(srcb, 2 * g + 1, nks);
-        } else {
-          a[q][2 * g - 4] = la.read(srca, 2 * g - 4, nks);
-          a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
-        }
         if constexpr (kAhead) {
           // first operand: one load per group over sub-steps 0 and 1;
           // second: two per group once the barrier has freed its slot
@@ -742,6 +735,14 @@ __device__ __forceinline__ void gemm_mainloop_direct(LA& la, LB& lb, int nk, cha
               lb.issue_part(slot_lds(sa), 2 * g + 1);
             }
           }
+        }
+        mma_row(acc, a[p][g], b[p], g, bf16{});
+        if (g < 2) {
+          b[q][2 * g] = lb.read(srcb, 2 * g, nks);
+          b[q][2 * g + 1] = lb.read(srcb, 2 * g + 1, nks);
+        } else {
+          a[q][2 * g - 4] = la.read(srca, 2 * g - 4, nks);
+          a[q][2 * g - 3] = la.read(srca, 2 * g - 3, nks);
         }
       }
       if (kAhead && ks == 1) {
