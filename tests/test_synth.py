@@ -32,7 +32,7 @@ def test_ignore_counts(name):
     assert np.all((case.labels[valid] >= 0) & (case.labels[valid] < case.cfg.V))
 
 
-def test_survey_valid_counts():
+def test_valid_row_counts_of_the_workloads():
     assert [CONFIGS[k].n_valid for k in ("c1", "c2", "c3", "c4", "c5")] == [230, 3891, 7782, 7782, 26214]
 
 
