@@ -21,6 +21,50 @@ constexpr size_t kHeaderBytes = 256;
 constexpr int64_t kVocabTile = 256;
 constexpr int64_t kRowTile = 256;
 
+// Split of grad_h = G W over the vocabulary (K = V: long K, narrow output),
+// so that the split tiles fill whole waves of the 256 CUs.  Among the splits
+// s <= s_max that leave >= 64 K steps per split (or s = 1), the best wave
+// efficiency (tiles * splits / (waves * 256), compared exactly); among
+// equally efficient ones, the smallest that gives at least 12 waves of tiles
+// still >= 256 K steps long, else the smallest.  (The last chunk of a call
+// holds only the valid rows left, often fewer token tiles: with few, long
+// waves its tiles fill the last wave poorly, with 12 or more the loss stays
+// small.)  `splits` counts the nonempty splits of `per` K steps each.
+struct SplitChoice {
+  int splits, per;
+};
+inline SplitChoice grad_h_split(int64_t tiles, int64_t ksteps, int64_t s_max) {
+  constexpr int64_t kCUs = 256, kMinSplitSteps = 64;
+  if (s_max > 16) s_max = 16;
+  if (s_max < 1) s_max = 1;
+  if (ksteps < 1) return SplitChoice{1, 1};
+  // the splits considered: s = 1, and s > 1 while >= 64 K steps per split
+  int64_t last = 1;
+  while (last < s_max && ksteps / (last + 1) >= kMinSplitSteps) ++last;
+  // best efficiency work / (waves * 256), kept as the pair (work, waves) and
+  // compared exactly by cross-multiplying
+  int64_t best_work = 0, best_waves = 1;
+  for (int64_t s = 1; s <= last; ++s) {
+    const int64_t per = (ksteps + s - 1) / s, work = tiles * ((ksteps + per - 1) / per);
+    const int64_t waves = (work + kCUs - 1) / kCUs;
+    if (s == 1 || work * best_waves > best_work * waves) {
+      best_work = work;
+      best_waves = waves;
+    }
+  }
+  int64_t pick = 0, pick_any = 0;
+  for (int64_t s = 1; s <= last && !pick; ++s) {
+    const int64_t per = (ksteps + s - 1) / s, real = (ksteps + per - 1) / per, work = tiles * real;
+    const int64_t waves = (work + kCUs - 1) / kCUs;
+    if (work * best_waves != best_work * waves) continue;
+    if (!pick_any) pick_any = s;
+    if (waves >= 12 && ksteps / real >= 256) pick = s;
+  }
+  if (!pick) pick = pick_any ? pick_any : 1;
+  const int64_t per = (ksteps + pick - 1) / pick;
+  return SplitChoice{(int)((ksteps + per - 1) / per), (int)per};
+}
+
 // Chunk plan and workspace layout (byte offsets from the workspace base).
 // A forward-only plan has no logits transient and no grad_h partials.
 struct Plan {

@@ -25,41 +25,14 @@ namespace flce {
 namespace {
 
 constexpr size_t kDefaultBudget = size_t(16) << 30;
-constexpr int64_t kCUs = 256;       // MI355X compute units (one 256x256 tile each)
-constexpr int64_t kMinSplitSteps = 64;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// grad_h = G W has K = vocabulary, long and narrow output: split K so that the
-// number of tiles fills whole waves of the 256 CUs.  Among the splits that
-// leave >= 64 K steps per split, take the best wave efficiency; among equally
-// efficient ones, the smallest that gives at least 12 waves of tiles still
-// >= 256 K steps long, else the smallest.  (The last chunk of a call holds
-// only the valid rows left, often fewer token tiles: with few, long waves its
-// tiles fill the last wave poorly, with 12 or more the loss stays small.)
+// grad_h = G W has K = vocabulary, long and narrow output: the split rule
+// (grad_h_split) applied to a full chunk of C rows, up to 16 splits.
 int64_t choose_split(int64_t C, int64_t H, int64_t Vp, int64_t es) {
   const int64_t tiles = ((C + kRowTile - 1) / kRowTile) * ((H + 255) / 256);
-  const int64_t ksteps = Vp * es / 128;
-  double eff[17] = {};
-  int64_t waves[17] = {}, real[17] = {};
-  double best_eff = 0.0;
-  int64_t last = 1;
-  for (int64_t s = 1; s <= 16; ++s) {
-    if (s > 1 && ksteps / s < kMinSplitSteps) break;
-    const int64_t per = (ksteps + s - 1) / s;
-    real[s] = (ksteps + per - 1) / per;
-    const int64_t work = tiles * real[s];
-    waves[s] = (work + kCUs - 1) / kCUs;
-    eff[s] = double(work) / double(waves[s] * kCUs);
-    if (eff[s] > best_eff) best_eff = eff[s];
-    last = s;
-  }
-  int64_t pick = 0;
-  for (int64_t s = 1; s <= last && !pick; ++s)
-    if (eff[s] >= best_eff - 1e-9 && waves[s] >= 12 && ksteps / real[s] >= 256) pick = s;
-  for (int64_t s = 1; s <= last && !pick; ++s)
-    if (eff[s] >= best_eff - 1e-9) pick = s;
-  return real[pick];
+  return grad_h_split(tiles, Vp * es / 128, 16).splits;
 }
 
 void layout(Plan* p) {
