@@ -317,6 +317,16 @@ int flce_scale_grads(const float* grad_scale, const void* grad_h_in, void* grad_
  */
 int flce_read_status(const void* workspace, hipStream_t stream);
 
+/*
+ * After a call, a workspace also holds N_valid, the call's number of rows
+ * whose label is not ignore_index, as a uint64 at byte offset
+ * FLCE_WS_N_VALID_OFFSET (device memory, written on the call's stream, valid
+ * until the next call that uses the workspace).  Token accuracy (Muse Glimmer
+ * page, Summary item 2) is n_correct / N_valid.  The status word read by
+ * flce_read_status is the int32 at byte 0.
+ */
+#define FLCE_WS_N_VALID_OFFSET 8
+
 /* Static, human-readable text for a return code. */
 const char* flce_strerror(int code);
 

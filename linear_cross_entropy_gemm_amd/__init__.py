@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     FLCE_REDUCTION_SUM,
     KERNEL_KINDS,
     NOALLOC_SCRATCH_BYTES,
+    WS_N_VALID_OFFSET,
     FlceError,
     flce_cross_entropy,
     flce_cross_entropy_workspace_size,
@@ -54,4 +55,5 @@ from .torch_api import (  # noqa: F401
     logits,
     read_status,
     scale_grads,
+    token_accuracy,
 )

@@ -27,6 +27,9 @@ FLCE_ELABEL = 4
 FLCE_EUNSUPPORTED = 5
 FLCE_ESCRATCH = 6
 
+# Byte offset of N_valid (uint64) in a workspace after a call (FLCE_WS_N_VALID_OFFSET).
+WS_N_VALID_OFFSET = 8
+
 # Static scratch of flce_fwd_bwd_noalloc (FLCE_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 256 << 20
 

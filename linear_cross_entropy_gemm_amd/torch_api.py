@@ -25,6 +25,7 @@ class FlceOutputs:
     loss_rows: Optional[torch.Tensor] = None   # [N] fp32 (row outputs / reduction "none")
     lse_rows: Optional[torch.Tensor] = None    # [N] fp32
     pred_rows: Optional[torch.Tensor] = None   # [N] int64, predicted token of every row
+    n_valid: Optional[torch.Tensor] = None     # [] int64 view of the workspace: rows not ignored
 
 
 @dataclasses.dataclass
@@ -35,6 +36,22 @@ class FlceForward:
     loss_rows: Optional[torch.Tensor] = None
     lse_rows: Optional[torch.Tensor] = None
     pred_rows: Optional[torch.Tensor] = None
+    n_valid: Optional[torch.Tensor] = None
+
+
+def _n_valid_view(workspace: torch.Tensor) -> torch.Tensor:
+    """N_valid of the last call that used ``workspace``, as a 0-d int64 view of
+    the device memory the call wrote it to (FLCE_WS_N_VALID_OFFSET): no copy,
+    no synchronisation; the next call on the workspace overwrites it."""
+    o = _lib.WS_N_VALID_OFFSET
+    return workspace[o:o + 8].view(torch.int64).reshape(())
+
+
+def token_accuracy(out) -> torch.Tensor:
+    """n_correct / N_valid (Muse Glimmer page, Summary item 2) of a ``fwd_bwd``
+    or ``forward`` result, as a 0-d float64 device tensor (0 when every row is
+    ignored); read it before the workspace is used again."""
+    return out.n_correct.to(torch.float64) / torch.clamp(out.n_valid, min=1).to(torch.float64)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -184,6 +201,7 @@ def fwd_bwd(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
     if out.loss_rows is not None and reduction == "none":
         out.loss_rows = out.loss_rows.reshape(labels.shape)
     out.workspace = workspace
+    out.n_valid = _n_valid_view(workspace)
     return out
 
 
@@ -229,6 +247,7 @@ def forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, ignore_index
             raise _lib.FlceError(st, "flce_fwd (device status)")
     if reduction == "none":
         res.loss_rows = res.loss_rows.reshape(labels.shape)
+    res.n_valid = _n_valid_view(workspace)
     return res
 
 

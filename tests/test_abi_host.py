@@ -403,3 +403,32 @@ def test_plan_budget_shrinks_the_split_before_the_chunk():
     b = L.flce_plan(N, H, V, 0, a.workspace_bytes - 1)
     assert b.chunk_rows == a.chunk_rows and b.split_k < a.split_k
     assert b.workspace_bytes <= a.workspace_bytes - 1
+
+
+def test_n_valid_offset_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "flce.h")).read()
+    m = re.search(r"#define\s+FLCE_WS_N_VALID_OFFSET\s+(\d+)", text)
+    assert m and int(m.group(1)) == L.WS_N_VALID_OFFSET
+
+
+def test_n_valid_view_reads_the_workspace_bytes():
+    """The token-accuracy denominator is a view of the workspace bytes the
+    device writes (no copy): on a host tensor, the view reads what sits at
+    FLCE_WS_N_VALID_OFFSET, and token_accuracy divides by it (0 / 0 -> 0)."""
+    import torch
+    from linear_cross_entropy_gemm_amd import torch_api
+    ws = torch.zeros(256, dtype=torch.uint8)
+    o = L.WS_N_VALID_OFFSET
+    ws[o:o + 8] = torch.tensor([7782], dtype=torch.int64).view(torch.uint8)
+    nv = torch_api._n_valid_view(ws)
+    assert nv.dim() == 0 and int(nv) == 7782
+    ws[o:o + 8] = torch.tensor([41], dtype=torch.int64).view(torch.uint8)
+    assert int(nv) == 41   # a view: the next call's value shows through
+
+    class R:
+        n_correct = torch.tensor(10, dtype=torch.int64)
+        n_valid = nv
+    assert float(L.token_accuracy(R)) == 10 / 41
+    ws[o:o + 8] = 0
+    R.n_correct = torch.tensor(0, dtype=torch.int64)
+    assert float(L.token_accuracy(R)) == 0.0

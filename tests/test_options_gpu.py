@@ -78,6 +78,11 @@ def test_forward_only(cid, base, N, H, V, T, m, red):
                                      ref["valid"])
     assert lo <= int(f.n_correct.item()) <= hi
     check_rows(case, ref, f.loss_rows, f.lse_rows, f.pred_rows)
+    # N_valid from the workspace, and token accuracy n_correct / N_valid, for both entry points
+    n_valid = int(np.sum(case.labels != IGN))
+    for res in (f, o):
+        assert int(res.n_valid.item()) == n_valid
+        assert float(L.token_accuracy(res).item()) == int(res.n_correct.item()) / max(n_valid, 1)
     # the same kernels compute each row's statistics on both entry points
     assert f.loss.item() == o.loss.item()
     assert int(f.n_correct.item()) == int(o.n_correct.item())
@@ -92,6 +97,7 @@ def test_forward_only(cid, base, N, H, V, T, m, red):
     assert fp.lse_rows is None and fp.pred_rows is None
     assert fp.loss.item() == op.loss.item()
     assert int(fp.n_correct.item()) == int(f.n_correct.item()) == int(op.n_correct.item())
+    assert int(fp.n_valid.item()) == int(op.n_valid.item()) == n_valid
     assert abs(fp.loss.item() - loss) <= 1e-6 * abs(loss)
 
 

@@ -144,6 +144,8 @@ def test_all_rows_ignored(base):
     assert float(o.loss.item()) == 0.0 and int(o.n_correct.item()) == 0
     assert not o.grad_h.float().abs().max().item()
     assert not o.grad_W.abs().max().item()
+    import linear_cross_entropy_gemm_amd as L
+    assert int(o.n_valid.item()) == 0 and float(L.token_accuracy(o).item()) == 0.0
 
 
 def test_empty_batch():
