@@ -262,6 +262,10 @@ extern "C" int flce_cross_entropy(const void* logits, int64_t ld_logits, const i
   return flce::run_cross_entropy(a, stream);
 }
 
+// The workspace header's fields sit where flce.h documents them.
+static_assert(offsetof(flce::Header, status) == 0, "status word at byte 0");
+static_assert(offsetof(flce::Header, n_valid) == FLCE_WS_N_VALID_OFFSET, "N_valid at FLCE_WS_N_VALID_OFFSET");
+
 extern "C" int flce_read_status(const void* workspace, hipStream_t stream) {
   if (!workspace) return FLCE_EINVAL;
   flce::Header hdr;

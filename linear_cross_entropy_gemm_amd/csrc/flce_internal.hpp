@@ -17,8 +17,6 @@ struct Header {
   unsigned long long n_valid;  // non-ignored rows of the call
 };
 
-static_assert(offsetof(Header, n_valid) == FLCE_WS_N_VALID_OFFSET, "N_valid sits where flce.h says");
-
 constexpr size_t kHeaderBytes = 256;
 constexpr int64_t kVocabTile = 256;
 constexpr int64_t kRowTile = 256;
