@@ -9,8 +9,9 @@ in HBM when the timed region starts.
 
 Prints one JSON line (rank 0) with the metric, a roofline entry for the
 dominant kernel (its average launch duration measured with HIP events on its
-own stream during the timed steps) and the fp64 oracle timed on a bounded
-sample of the same workload on the host cores.
+own stream during the timed steps), every kernel's time per step (each GEMM
+also as TFLOP/s and fraction of the dense peak) and the fp64 oracle timed on
+a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -349,6 +350,11 @@ def main() -> int:
     # launches together process N_valid token rows; the materialised logits
     # GEMM processes all N.
     rows_alg = cfg.n_valid if args.entry in ("fwd_bwd", "fwd") else cfg.N
+    for k in kernels:
+        if k in GEMM_KINDS:   # every GEMM does 2 * rows * H * V per step over its launches
+            tf = 2.0 * rows_alg * cfg.H * cfg.V / (kernels[k]["ms_per_step"] * 1e-3) / 1e12
+            kernels[k]["tflops"] = tf
+            kernels[k]["frac_of_peak"] = tf / peak
     flops_per_launch = 2.0 * rows_alg * cfg.H * cfg.V / kernels[dom]["launches_per_step"]
     achieved = flops_per_launch / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
     traffic = stored_traffic(dom, args.config)
